@@ -1,0 +1,111 @@
+/*
+ * CPU oracle for the wave-index build and decode.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is a plain, slow, scalar reading of the
+ * method described on the RetroInfer pages (framerc blog "KV缓存技术与
+ * RetroInfer系统...", sections 2.1-3.3; techwalker article, section 3;
+ * gist.science summary, "Technische Samenvatting" section 2A). Only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg may load it.
+ * It shares no code, header or table with the HIP library and must never be
+ * used as a fallback for it.
+ *
+ * All tensors are passed as float32 arrays whose values are exactly the
+ * stored dtype values (bf16 values are exact in float32). Floating-point
+ * results that the method defines as averages or sums are produced in the
+ * precision stated at each function.
+ */
+#ifndef WI_ORACLE_H
+#define WI_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtypes. */
+enum { WIO_F32 = 0, WIO_BF16 = 1 };
+
+typedef struct {
+  int32_t dtype;
+  int32_t batch, n_kv_heads, head_dim;
+  int64_t n_ctx;
+  int32_t seg_len, clusters_per_seg, n_sink, n_local, n_iters;
+  uint64_t seed;
+  uint32_t layer_id;
+} wio_desc;
+
+typedef struct {
+  int32_t n_q_heads;
+  int32_t k_retrieve, k_estimate;
+  double scale; /* 0 -> 1/sqrt(head_dim) */
+} wio_ddesc;
+
+/* ---- partition ------------------------------------------------------- */
+/* Number of segments of one unit, clusters per unit, and the block
+ * capacity per unit (an upper bound on sum_c ceil(n_c / T)). Returns 0 on
+ * success, -1 on invalid sizes. */
+int wio_sizes(const wio_desc *d, int64_t *n_segments, int64_t *n_clusters,
+              int64_t *block_cap, int32_t *tokens_per_block);
+
+/* ---- counter-based random numbers ------------------------------------ */
+uint64_t wio_mix64(uint64_t z);
+uint64_t wio_key(uint64_t seed, uint64_t b, uint64_t l, uint64_t h,
+                 uint64_t s, uint64_t r);
+
+/* ---- rounding and distances ------------------------------------------ */
+float wio_round_bf16(float x);
+float wio_dist32(const float *x, const float *c, int d);
+double wio_dist64(const float *x, const float *c, int d);
+
+/* ---- k-means pieces on one segment ------------------------------------ */
+void wio_kmeanspp(const float *X, int n, int d, int k, uint64_t seed,
+                  uint64_t b, uint64_t l, uint64_t h, uint64_t s,
+                  int32_t *picks);
+void wio_assign(const float *X, int n, int d, const float *C, int k,
+                int32_t *a);
+void wio_update(const float *X, int n, int d, const int32_t *a, int k,
+                int dtype, float *C, int32_t *counts);
+
+/* ---- full build ------------------------------------------------------- */
+/* K, V: [B][H][N][d]. init: [B][H][C][d] or NULL (k-means++).
+ * Outputs per unit u = b*H + h:
+ *   centroids [U][C][d], sizes [U][C], vsum [U][C][d],
+ *   block_off [U][C+1], kblk/vblk [U][cap*T][d], slot_token [U][cap*T],
+ *   steady_k/steady_v [U][n_sink+n_local][d], assign [U][n_idx]. */
+int wio_build(const wio_desc *d, const float *K, const float *V,
+              const float *init, float *centroids, int32_t *sizes,
+              float *vsum, int32_t *block_off, float *kblk, float *vblk,
+              int32_t *slot_token, float *steady_k, float *steady_v,
+              int32_t *assign);
+
+/* ---- decode ----------------------------------------------------------- */
+/* q: [B][Hq][d]. out: [B][Hq][d] (fp64). sel: [U][K_r + K_e'] cluster ids
+ * in rank order (K_e' = min(K_e, C - K_r)); exec_tokens: [U][exec_cap]
+ * (token positions, steady then retrieved clusters in rank order);
+ * n_exec: [U]. gkey: [U][C] exact group-summed scores or NULL.
+ * Returns 0, or -1 when K_r > C. */
+int wio_decode(const wio_desc *d, const wio_ddesc *dd, const float *centroids,
+               const int32_t *sizes, const float *vsum,
+               const int32_t *block_off, const float *kblk, const float *vblk,
+               const int32_t *slot_token, const float *steady_k,
+               const float *steady_v, const float *q, double *out,
+               int32_t *sel, int32_t *exec_tokens, int32_t *n_exec,
+               int64_t exec_cap, double *gkey);
+
+/* Tripartite attention for given retrieval set R [U][n_r] and estimation
+ * set E [U][n_e] (cluster ids), fp64. Used to check a selection made
+ * elsewhere once that selection has been validated. */
+int wio_attend_sets(const wio_desc *d, const wio_ddesc *dd,
+                    const float *centroids, const int32_t *sizes,
+                    const float *vsum, const int32_t *block_off,
+                    const float *kblk, const float *vblk,
+                    const float *steady_k, const float *steady_v,
+                    const float *q, const int32_t *R, int32_t n_r,
+                    const int32_t *E, int32_t n_e, double *out);
+
+int wio_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
