@@ -1,0 +1,234 @@
+"""Benchmark: wave-index decode attention on one MI355X.
+
+Workload: the Llama3.1-8B-shaped layer at 128K context (32 query / 8 KV heads,
+head_dim 128, bf16, batch 1, 16 segments x 8K tokens, 512 clusters per
+segment, retrieval 1.8 %, estimation 23 %, steady 4 + 64), seeded synthetic
+clustered keys (see sparse_long_context_segmented_amd/synth.py).
+
+A timed step is one wi_decode_attention call (score, select, gather + exact
+attention, estimation, merge) for every sequence of the batch; value =
+decode queries per second per layer (batch / step time). Inputs (the index
+built by wi_build_index from the seeded K/V, and the queries) are resident in
+HBM before timing; steps rotate over R copies of the index at distinct
+addresses so the 256 MB last-level cache cannot serve repeated steps. The
+index build is timed in the same run and reported beside it ("build").
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b-128k-b1")
+    ap.add_argument("--instances", type=int, default=16,
+                    help="index copies the steps rotate over")
+    ap.add_argument("--build-reps", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bound on the oracle's timed CPU work")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for rocprofv3 (no CPU leg, few steps)")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
+              "(the path shards by KV head / sequence with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_long_context_segmented_amd import synth, wi
+
+    w = next(x for x in synth.WORKLOADS if x.name == a.workload)
+    if a.profile:
+        a.steps, a.warmup, a.no_cpu, a.build_reps = min(a.steps, 20), 5, True, 1
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs: seeded synthetic K, V, q (host), then resident in HBM ----
+    t0 = time.time()
+    K, V, q = synth.gen_batch(w)
+    gen_s = time.time() - t0
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    kt = torch.from_numpy(K).to(dev, dt)
+    vt = torch.from_numpy(V).to(dev, dt)
+    qt = torch.from_numpy(q).to(dev, dt)
+    desc = wi.make_desc(w.dtype, w.batch, w.n_kv_heads, w.n_ctx, seg_len=w.seg_len,
+                        clusters_per_seg=w.clusters_per_seg, n_iters=w.n_iters)
+    ns, C, cap, wsb = wi.index_sizes(desc)
+    U = w.batch * w.n_kv_heads
+    e = 2 if w.dtype == "bf16" else 4
+
+    # ---- build leg ----
+    ws_build = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ix = wi.alloc_index(desc, dev)
+    wi.build_index(desc, kt, vt, index=ix, ws=ws_build)  # warm
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    build_ms = []
+    for _ in range(a.build_reps):
+        ev0.record(stream)
+        wi.build_index(desc, kt, vt, index=ix, ws=ws_build)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        build_ms.append(ev0.elapsed_time(ev1))
+    wi.timing_start()
+    wi.build_index(desc, kt, vt, index=ix, ws=ws_build)
+    brec = wi.timing_stop()
+    bk = {}
+    for name, ms in brec:
+        bk.setdefault(name, []).append(ms)
+    n_assign = len(bk.get("assign", []))
+    assign_ms = float(np.mean(bk["assign"])) if n_assign else float("nan")
+    # assignment FLOPs per launch: 2 * n_s * C_s * 128 summed over segments
+    seg_n = [min(w.seg_len, (w.n_ctx - 68) - s * w.seg_len) for s in range(ns)]
+    flops = sum(2.0 * n * min(w.clusters_per_seg, n) * 128 for n in seg_n) * U
+    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    assign_tflops = flops / (assign_ms * 1e-3) / 1e12
+    build = {
+        "ms": round(float(np.median(build_ms)), 3),
+        "phase_ms": {k: round(float(np.sum(v)), 3) for k, v in bk.items()},
+        "assign": {"bound": "mfma", "achieved": round(assign_tflops, 2),
+                   "peak": peak_mfma, "unit": "TFLOP/s",
+                   "frac": round(assign_tflops / peak_mfma, 4),
+                   "ms_per_launch": round(assign_ms, 4), "launches": n_assign},
+    }
+    del kt, vt, ws_build
+
+    # ---- decode: R index copies at distinct addresses ----
+    k_r, k_e = w.budgets()
+    dd = wi.DecodeDesc(w.n_q_heads, k_r, k_e, 0.0)
+    nexe = torch.empty(U, dtype=torch.int32, device=dev)
+    wi.decode_attention(ix, dd, qt, n_exec=nexe)
+    torch.cuda.synchronize()
+    retrieved = int((nexe.cpu().numpy() - 68).sum())  # sum over units of sum_R n_c
+    copies = [ix]
+    for _ in range(a.instances - 1):
+        copies.append(wi.Index(desc, *[getattr(ix, f).clone() for f in (
+            "centroids", "cluster_size", "value_sum", "block_off", "k_blocks", "v_blocks",
+            "slot_token", "steady_k", "steady_v", "assign")]))
+    wsd = torch.empty(wi.decode_sizes(desc, dd), dtype=torch.uint8, device=dev)
+    outs = [torch.empty(w.batch, w.n_q_heads, 128, dtype=torch.float32, device=dev)
+            for _ in range(len(copies))]
+    for i in range(a.warmup):
+        wi.decode_attention(copies[i % len(copies)], dd, qt, out=outs[i % len(copies)], ws=wsd)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    t_start = time.perf_counter()
+    for i in range(a.steps):
+        j = i % len(copies)
+        wi.decode_attention(copies[j], dd, qt, out=outs[j], ws=wsd)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_ms = ev0.elapsed_time(ev1) / a.steps
+
+    # per-kernel durations over the same number of steps (timing hook)
+    wi.timing_start()
+    for i in range(a.steps):
+        j = i % len(copies)
+        wi.decode_attention(copies[j], dd, qt, out=outs[j], ws=wsd)
+    recs = wi.timing_stop()
+    kt_ms = {}
+    for name, ms in recs:
+        kt_ms.setdefault(name, []).append(ms)
+    avg = {k: float(np.mean(v)) for k, v in kt_ms.items()}
+
+    # algorithmic bytes per step (each unit): centroids, E value sums, metadata,
+    # retrieved K/V (measured sum of R cluster sizes), steady K/V, q, out
+    G = w.group
+    k_e_eff = min(k_e, C - k_r)
+    b_score = U * (C * 128 * e + G * 128 * e)
+    b_attend = (U * (k_e_eff * 128 * 4 + (k_r + k_e_eff) * 4 + k_r * 8 + 68 * 128 * e * 2)
+                + retrieved * 128 * e * 2)
+    b_out = U * G * 128 * 4
+    step_bytes = b_score + b_attend + b_out
+    per_kernel = {"score": b_score, "attend": b_attend, "combine": b_out, "select": 0}
+    dom = max(avg, key=lambda k: avg[k])
+    dom_bytes = per_kernel.get(dom, 0)
+    achieved = dom_bytes / (avg[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None,
+                "kernel_ms": {k: round(v, 5) for k, v in avg.items()},
+                "algorithmic_bytes": {k: int(v) for k, v in per_kernel.items()}}
+
+    qps = w.batch * a.steps / (step_ms * a.steps * 1e-3)
+    res = {
+        "metric": "decode attention queries/s per layer at 128K ctx; achieved HBM GB/s vs peak",
+        "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.n_ctx,
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128,
+                   "seg_len": w.seg_len, "clusters_per_seg": w.clusters_per_seg,
+                   "k_retrieve": k_r, "k_estimate": k_e_eff, "index_copies": len(copies)},
+        "step_hbm_GBps": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+        "step_bytes": int(step_bytes),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "build": build,
+        "gen_s": round(gen_s, 1),
+    }
+
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, K, V, q, k_r, k_e, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, K, V, q, k_r, k_e, seconds):
+    """The oracle, untuned, on a bounded sample: one KV head (unit h = 0) of the
+    same workload, built once and decoded repeatedly for about `seconds`;
+    a decode step of the full layer is that unit's time x (units per step)."""
+    import oracle
+    oracle.compile_oracle()
+    cores = oracle.num_threads()
+    od = oracle.make_desc(w.dtype, 1, 1, w.n_ctx, seg_len=w.seg_len,
+                          clusters_per_seg=w.clusters_per_seg, n_iters=w.n_iters)
+    K1, V1 = K[:1, :1], V[:1, :1]
+    t0 = time.perf_counter()
+    idx = oracle.build(od, K1, V1)
+    build_s = time.perf_counter() - t0
+    q1 = q[:1, :w.group]
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode(od, w.group, k_r, k_e, idx, q1)
+        n += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    per_unit = (time.perf_counter() - t0) / n
+    units = w.batch * w.n_kv_heads
+    step = per_unit * units
+    return {"value": round(w.batch / step, 2), "unit": "queries/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"unit (b=0, h=0) of {units}: oracle build once ({build_s:.1f} s) "
+                      f"and {n} decode steps; step = unit time x {units}",
+            "decode_ms_per_unit": round(per_unit * 1e3, 2),
+            "build_s_per_unit": round(build_s, 2),
+            "build_s_layer_extrapolated": round(build_s * units, 1)}
+
+
+if __name__ == "__main__":
+    main()

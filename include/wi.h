@@ -1,0 +1,208 @@
+/*
+ * wi.h -- C ABI of the wave-index library (libwi.so) for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Two operations, as the RetroInfer pages state the problem:
+ *
+ *   wi_build_index      cluster each KV head's keys independently per
+ *                       fixed-length segment (k-means), keep centroids,
+ *                       cluster sizes and per-cluster value sums, and lay
+ *                       the KV out cluster-contiguously in 2 KB blocks
+ *                       (framerc blog, section 2.1 "Wave索引" and its
+ *                       segmented_kmeans sketch; section 2.2, 2 KB physical
+ *                       blocks; section 3.1, one cluster's KV stored
+ *                       contiguously).
+ *
+ *   wi_decode_attention for one decode query per sequence: score every
+ *                       centroid, take the top clusters as the retrieval
+ *                       zone and the next tier as the estimation zone,
+ *                       attend exactly over the steady zone (first n_sink and
+ *                       last n_local tokens) plus the retrieved clusters'
+ *                       tokens, estimate the estimation zone from centroid
+ *                       score x cluster size and the cluster value sum, and
+ *                       merge the partial softmaxes (framerc blog section
+ *                       2.1 zones; section 2.2 sync path step 1, query the
+ *                       index for cluster ids; section 3.2 execution buffer;
+ *                       section 3.3 hybrid attention and merge; techwalker
+ *                       article section 3, the three zones).
+ *
+ * Conventions (all entry points):
+ *   - Every buffer is caller-owned device memory (except descriptors, which
+ *     are host structs). The library never allocates or frees memory, keeps
+ *     no state between calls and fully overwrites every output it is given,
+ *     padding included.
+ *   - All device work is enqueued on `stream` (NULL = default stream). Calls
+ *     return after enqueue without synchronising. Outputs are valid, and
+ *     inputs reusable, only after the caller synchronises the stream.
+ *   - Validation happens on the host before any HIP call; a call that fails
+ *     validation enqueues nothing.
+ *   - Pointers to device buffers must be 16-byte aligned.
+ *   - The same inputs and seed give bit-identical outputs on every run.
+ *   - Stateless: concurrent calls on different streams with disjoint
+ *     workspaces and outputs are safe.
+ *   - Device faults surface at the caller's next synchronisation.
+ */
+#ifndef WI_H
+#define WI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WI_OK = 0,
+  WI_E_INVALID = 1,     /* null required pointer, misalignment, bad sizes  */
+  WI_E_UNSUPPORTED = 2, /* head_dim != 128, unknown dtype, Hq % Hkv != 0   */
+  WI_E_WORKSPACE = 3,   /* workspace smaller than the sizes call reports   */
+  WI_E_HIP = 4          /* a HIP launch error; text in wi_last_error()     */
+} wi_status;
+
+enum { WI_F32 = 0, WI_BF16 = 1 };
+
+/* Index shape. One unit = (sequence b, KV head h) of one layer.
+ * Steady zone: positions [0, n_sink) and [n_ctx - n_local, n_ctx).
+ * Indexed tokens: [n_sink, n_ctx - n_local), cut into consecutive segments of
+ * seg_len tokens (the last one may be short); segment s has
+ * C_s = min(clusters_per_seg, n_s) clusters; cluster ids are contiguous by
+ * segment, so C = sum_s C_s clusters per unit.
+ * Tokens per 2 KB block: T = 2048 / (head_dim * bytes(dtype)) = 8 (bf16) or
+ * 4 (fp32). */
+typedef struct {
+  int32_t dtype;            /* WI_F32 or WI_BF16: keys, values, centroids, q */
+  int32_t batch;            /* B >= 1                                        */
+  int32_t n_kv_heads;       /* H >= 1                                        */
+  int32_t head_dim;         /* must be 128                                   */
+  int64_t n_ctx;            /* N >= n_sink + n_local + 1                     */
+  int32_t seg_len;          /* tokens per segment, 1..8192 (8192 = 8K)       */
+  int32_t clusters_per_seg; /* k, 1..512                                     */
+  int32_t n_sink;           /* leading steady tokens (4), >= 0               */
+  int32_t n_local;          /* trailing steady tokens (64), >= 0             */
+  int32_t n_iters;          /* Lloyd iterations after initialisation, >= 0   */
+  uint64_t seed;            /* k-means++ seed                                */
+  uint32_t layer_id;        /* mixed into the k-means++ random stream        */
+  int64_t kv_stride_b;      /* element strides of the K and V inputs         */
+  int64_t kv_stride_h;      /*   [B, H, N, head_dim]; head_dim contiguous;   */
+  int64_t kv_stride_t;      /*   all strides must be multiples of 8          */
+} wi_index_desc;
+
+/* Index buffers (device memory, caller-owned). C and cap come from
+ * wi_index_sizes; U = batch * n_kv_heads; n_idx = n_ctx - n_sink - n_local;
+ * n_st = n_sink + n_local.
+ *   centroids    [U][C][128] dtype   cluster means (rounded to dtype)
+ *   cluster_size [U][C] int32        members per cluster
+ *   value_sum    [U][C][128] float   sum of member values (fp64, rounded)
+ *   block_off    [U][C+1] int32      first block of each cluster; [C] = used
+ *   k_blocks     [U][cap][T][128]    keys, cluster-contiguous, 2 KB blocks
+ *   v_blocks     [U][cap][T][128]    values, same layout
+ *   slot_token   [U][cap*T] int32    token position of each slot, -1 = pad
+ *   steady_k     [U][n_st][128]      keys of the steady zone, in order
+ *   steady_v     [U][n_st][128]      values of the steady zone
+ *   assign       [U][n_idx] int32    cluster id of each indexed token
+ * Cluster c's members occupy slots [T*block_off[c], T*block_off[c] + size[c])
+ * in ascending position; remaining slots of its last block, and all blocks
+ * past block_off[C], hold token -1 and zero data. */
+typedef struct {
+  void *centroids;
+  int32_t *cluster_size;
+  float *value_sum;
+  int32_t *block_off;
+  void *k_blocks;
+  void *v_blocks;
+  int32_t *slot_token;
+  void *steady_k;
+  void *steady_v;
+  int32_t *assign;
+} wi_index_bufs;
+
+/* Host-only: sizes derived from the descriptor. Any output pointer may be
+ * NULL. Returns WI_E_INVALID / WI_E_UNSUPPORTED for a bad descriptor. */
+wi_status wi_index_sizes(const wi_index_desc *desc, int64_t *n_segments,
+                         int64_t *n_clusters, int64_t *block_cap,
+                         size_t *workspace_bytes);
+
+/* Build the index of every unit.
+ *   k, v          device [B][H][N][128] dtype, strides from desc
+ *   init_centroids NULL: k-means++ seeding per segment (first centroid
+ *                 uniform, then D^2 sampling; counter-based random stream
+ *                 keyed by (seed, b, layer_id, h, segment, round)).
+ *                 Non-NULL: device [U][C][128] dtype starting centroids.
+ *   Then n_iters Lloyd iterations (assign to the nearest centroid, lowest id
+ *   on ties; replace each non-empty cluster's centroid by the rounded mean
+ *   of its members). With n_iters = 0 the centroids stay at their initial
+ *   values and the membership is one assignment to them. The outputs are
+ *   the last assignment's membership and the last update's centroids.
+ *   ws            device workspace of >= workspace_bytes from
+ *                 wi_index_sizes; contents on entry are ignored.
+ */
+wi_status wi_build_index(const wi_index_desc *desc, const void *k,
+                         const void *v, const void *init_centroids,
+                         const wi_index_bufs *bufs, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Decode shape. Query head j maps to KV head j / (n_q_heads / n_kv_heads). */
+typedef struct {
+  int32_t n_q_heads;   /* multiple of n_kv_heads; G = Hq / Hkv <= 16      */
+  int32_t k_retrieve;  /* K_r: retrieval-zone clusters, 0 <= K_r <= C     */
+  int32_t k_estimate;  /* K_e: estimation-zone clusters, clamped to C-K_r */
+  float scale;         /* softmax scale; 0 -> 1/sqrt(head_dim)            */
+} wi_decode_desc;
+
+/* Host-only: workspace bytes for wi_decode_attention. */
+wi_status wi_decode_sizes(const wi_index_desc *desc,
+                          const wi_decode_desc *ddesc, size_t *workspace_bytes);
+
+/* One decode step for every sequence of the batch.
+ *   q            device [B][Hq][128] dtype
+ *   out          device [B][Hq][128] float32 attention output
+ *   Ranking: clusters of a unit are ranked by g_c = sum over the unit's query
+ *   heads of <q_j, centroid_c> (float32), larger first, lower id on ties.
+ *   Ranks [0, K_r) form the retrieval zone R, the next
+ *   min(K_e, C - K_r) ranks the estimation zone E. For each query head j:
+ *     out_j = (sum_{i in steady + members(R)} e^{z_i} v_i
+ *              + sum_{c in E, n_c > 0} e^{s_c} VS_c)
+ *           / (sum_{i} e^{z_i} + sum_{c in E, n_c > 0} n_c e^{s_c}),
+ *   z_i = scale <q_j, k_i>, s_c = scale <q_j, centroid_c>.
+ * Optional debug outputs (written only when non-NULL):
+ *   sel_ids      device [U][K_r + K_e'] cluster ids in rank order
+ *   exec_tokens  device [U][exec_cap] token positions of the execution
+ *                buffer: steady positions in order, then each retrieved
+ *                cluster's members (rank order, ascending position);
+ *                entries past exec_cap are dropped; needs slot_token
+ *   n_exec       device [U] execution-buffer length (may exceed exec_cap)
+ *   bufs->assign is not read; bufs->slot_token only for exec_tokens.
+ */
+wi_status wi_decode_attention(const wi_index_desc *desc,
+                              const wi_decode_desc *ddesc,
+                              const wi_index_bufs *bufs, const void *q,
+                              float *out, int32_t *sel_ids,
+                              int32_t *exec_tokens, int32_t *n_exec,
+                              int64_t exec_cap, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Measurement hook. wi_timing_start() makes every kernel launch issued by
+ * this library on the calling thread be bracketed by two HIP events recorded
+ * on the launch's own stream, until wi_timing_stop(). wi_timing_stop()
+ * synchronises those events and writes, for up to max_records launches in
+ * issue order, the kernel's name id (see wi_kernel_name) and its duration in
+ * milliseconds; it returns the number of launches recorded (which may exceed
+ * max_records) or -1 on a HIP error. Timing adds an event pair per launch and
+ * is meant for measurement runs only. */
+wi_status wi_timing_start(void);
+int32_t wi_timing_stop(int32_t max_records, int32_t *name_ids, float *ms);
+const char *wi_kernel_name(int32_t name_id);
+
+/* Human-readable name of a status code (static storage). */
+const char *wi_status_str(wi_status s);
+
+/* Message of the last failed call on this thread (thread-local storage;
+ * empty string if none). */
+const char *wi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WI_H */

@@ -64,7 +64,7 @@ def lib():
         _lib.wio_kmeanspp.argtypes = [P, i32, i32, i32, u64, u64, u64, u64, u64, P]
         _lib.wio_assign.argtypes = [P, i32, i32, P, i32, P]
         _lib.wio_update.argtypes = [P, i32, i32, P, i32, i32, P, P]
-        _lib.wio_build.argtypes = [P] * 14
+        _lib.wio_build.argtypes = [P] * 15
         _lib.wio_decode.argtypes = [P] * 16 + [i64, P]
         _lib.wio_attend_sets.argtypes = [P] * 11 + [P, i32, P, i32, P]
         _lib.wio_num_threads.restype = ctypes.c_int
@@ -129,8 +129,11 @@ def update(X, a, C, dtype):
     return C, cnt
 
 
-def build(desc, K, V, init=None):
-    """K, V: [B, H, N, d] float32. Returns a dict of index arrays."""
+def build(desc, K, V, init=None, units=None):
+    """K, V: [B, H, N, d] float32. Returns a dict of index arrays.
+
+    units: optional list of unit ids (b * H + h) to build; other units'
+    outputs are left uninitialised."""
     ns, C, cap, T = sizes(desc)
     U = desc.batch * desc.n_kv_heads
     d = desc.head_dim
@@ -141,6 +144,10 @@ def build(desc, K, V, init=None):
     assert K.shape == (desc.batch, desc.n_kv_heads, desc.n_ctx, d)
     if init is not None:
         init = np.ascontiguousarray(init, dtype=np.float32).reshape(U, C, d)
+    mask = None
+    if units is not None:
+        mask = np.zeros(U, np.uint8)
+        mask[list(units)] = 1
     out = dict(
         centroids=np.empty((U, C, d), np.float32), sizes=np.empty((U, C), np.int32),
         vsum=np.empty((U, C, d), np.float32), block_off=np.empty((U, C + 1), np.int32),
@@ -152,7 +159,7 @@ def build(desc, K, V, init=None):
                          _p(out["centroids"]), _p(out["sizes"]), _p(out["vsum"]),
                          _p(out["block_off"]), _p(out["kblk"]), _p(out["vblk"]),
                          _p(out["slot_token"]), _p(out["steady_k"]), _p(out["steady_v"]),
-                         _p(out["assign"]))
+                         _p(out["assign"]), _p(mask))
     if rc != 0:
         raise ValueError("oracle build failed")
     return out

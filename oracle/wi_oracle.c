@@ -259,7 +259,7 @@ int wio_build(const wio_desc *d, const float *K, const float *V,
               const float *init, float *centroids, int32_t *sizes,
               float *vsum, int32_t *block_off, float *kblk, float *vblk,
               int32_t *slot_token, float *steady_k, float *steady_v,
-              int32_t *assign) {
+              int32_t *assign, const unsigned char *unit_mask) {
   int64_t ns, C, cap;
   int32_t T;
   if (wio_sizes(d, &ns, &C, &cap, &T) != 0) return -1;
@@ -280,6 +280,7 @@ int wio_build(const wio_desc *d, const float *K, const float *V,
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t job = 0; job < U * ns; job++) {
     int64_t u = job / ns, s = job % ns;
+    if (unit_mask && !unit_mask[u]) continue;
     int64_t b = u / d->n_kv_heads, h = u % d->n_kv_heads;
     int64_t start = d->n_sink + s * d->seg_len;
     int n = (int)seg_len_of(d, s);
@@ -315,6 +316,7 @@ int wio_build(const wio_desc *d, const float *K, const float *V,
   /* Layout and value sums, one unit at a time. */
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t u = 0; u < U; u++) {
+    if (unit_mask && !unit_mask[u]) continue;
     const int32_t *cnt = sizes + (size_t)u * C;
     int32_t *bo = block_off + (size_t)u * (C + 1);
     bo[0] = 0;
@@ -472,13 +474,16 @@ int wio_decode(const wio_desc *d, const wio_ddesc *dd, const float *centroids,
     const float *qg = q + ((size_t)b * dd->n_q_heads + (size_t)h * G) * D;
     /* Score ([blog] 2.2: query the wave index for cluster ids). Reading:
      * one selection per KV head, keyed by the sum over its query heads of
-     * <q_h, centroid>; this ranks like the scaled logit sum. */
+     * <q_h, centroid>; this ranks like the scaled logit sum. The key is that
+     * sum computed in float64 (exact for bf16 data) and rounded once to
+     * float32, the precision the ranking is taken in; equal keys go to the
+     * lower cluster id. */
     ranked *rk = (ranked *)malloc(sizeof(ranked) * (size_t)C);
     for (int64_t c = 0; c < C; c++) {
       double g = 0.0;
       for (int j = 0; j < G; j++)
         g += dot64(qg + (size_t)j * D, centroids + ((size_t)u * C + c) * D, D);
-      rk[c].g = g;
+      rk[c].g = (double)(float)g;
       rk[c].id = (int32_t)c;
       if (gkey) gkey[(size_t)u * C + c] = g;
     }

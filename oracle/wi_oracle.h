@@ -71,12 +71,14 @@ void wio_update(const float *X, int n, int d, const int32_t *a, int k,
  * Outputs per unit u = b*H + h:
  *   centroids [U][C][d], sizes [U][C], vsum [U][C][d],
  *   block_off [U][C+1], kblk/vblk [U][cap*T][d], slot_token [U][cap*T],
- *   steady_k/steady_v [U][n_sink+n_local][d], assign [U][n_idx]. */
+ *   steady_k/steady_v [U][n_sink+n_local][d], assign [U][n_idx].
+ * unit_mask: [U] or NULL; units with a zero entry are skipped (their
+ * outputs are left untouched). */
 int wio_build(const wio_desc *d, const float *K, const float *V,
               const float *init, float *centroids, int32_t *sizes,
               float *vsum, int32_t *block_off, float *kblk, float *vblk,
               int32_t *slot_token, float *steady_k, float *steady_v,
-              int32_t *assign);
+              int32_t *assign, const unsigned char *unit_mask);
 
 /* ---- decode ----------------------------------------------------------- */
 /* q: [B][Hq][d]. out: [B][Hq][d] (fp64). sel: [U][K_r + K_e'] cluster ids

@@ -1,0 +1,389 @@
+// C ABI of libwi.so (declared in include/wi.h): host-side validation,
+// sizes, workspace carving and the stream-ordered launch sequences of the
+// index build and the decode step.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "wi_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+wi_status fail(wi_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+wi_status hip_fail(hipError_t e, const char* where) {
+  return fail(WI_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+// Validate the index descriptor and derive the call geometry.
+wi_status make_geom(const wi_index_desc* d, wi::Geom* g) {
+  if (!d) return fail(WI_E_INVALID, "desc is NULL");
+  if (d->dtype != WI_F32 && d->dtype != WI_BF16)
+    return fail(WI_E_UNSUPPORTED, "unknown dtype %d", d->dtype);
+  if (d->head_dim != wi::D) return fail(WI_E_UNSUPPORTED, "head_dim %d != 128", d->head_dim);
+  if (d->batch < 1 || d->n_kv_heads < 1)
+    return fail(WI_E_INVALID, "batch %d / n_kv_heads %d must be >= 1", d->batch, d->n_kv_heads);
+  if (d->n_sink < 0 || d->n_local < 0)
+    return fail(WI_E_INVALID, "n_sink %d / n_local %d must be >= 0", d->n_sink, d->n_local);
+  if (d->n_ctx < (int64_t)d->n_sink + d->n_local + 1)
+    return fail(WI_E_INVALID, "n_ctx %lld must be >= n_sink + n_local + 1", (long long)d->n_ctx);
+  if (d->n_ctx >= (int64_t(1) << 31)) return fail(WI_E_INVALID, "n_ctx too large");
+  if (d->seg_len < 1 || d->seg_len > wi::MAX_SEG)
+    return fail(WI_E_INVALID, "seg_len %d outside [1, %d]", d->seg_len, wi::MAX_SEG);
+  if (d->clusters_per_seg < 1 || d->clusters_per_seg > wi::MAX_K)
+    return fail(WI_E_INVALID, "clusters_per_seg %d outside [1, %d]", d->clusters_per_seg,
+                wi::MAX_K);
+  if (d->n_iters < 0) return fail(WI_E_INVALID, "n_iters %d < 0", d->n_iters);
+  if (d->kv_stride_t <= 0 || d->kv_stride_h < 0 || d->kv_stride_b < 0 ||
+      d->kv_stride_t % 8 || d->kv_stride_h % 8 || d->kv_stride_b % 8)
+    return fail(WI_E_INVALID, "K/V strides must be non-negative multiples of 8 (t > 0)");
+  wi::Geom& G = *g;
+  G.dtype = d->dtype;
+  G.B = d->batch;
+  G.H = d->n_kv_heads;
+  G.U = d->batch * d->n_kv_heads;
+  G.N = d->n_ctx;
+  G.n_sink = d->n_sink;
+  G.n_local = d->n_local;
+  G.n_st = d->n_sink + d->n_local;
+  G.n_idx = d->n_ctx - G.n_st;
+  G.seg_len = d->seg_len;
+  G.kk = d->clusters_per_seg;
+  G.n_seg = (int)((G.n_idx + G.seg_len - 1) / G.seg_len);
+  int64_t C = 0;
+  for (int s = 0; s < G.n_seg; s++) C += wi::seg_c(G, s);
+  if ((int64_t)G.U * G.n_idx >= (int64_t(1) << 31) || (int64_t)G.U * C >= (int64_t(1) << 31))
+    return fail(WI_E_INVALID, "batch * heads * tokens exceeds 2^31");
+  G.C = (int)C;
+  G.T = 2048 / (wi::D * (d->dtype == WI_BF16 ? 2 : 4));
+  G.cap = (G.n_idx + C * (G.T - 1)) / G.T;
+  G.sb = d->kv_stride_b;
+  G.sh = d->kv_stride_h;
+  G.st = d->kv_stride_t;
+  G.seed = d->seed;
+  G.layer = d->layer_id;
+  G.n_iters = d->n_iters;
+  int cmax = G.kk < G.seg_len ? G.kk : G.seg_len;
+  if ((int64_t)cmax > G.n_idx) cmax = (int)G.n_idx;
+  G.cmax = cmax;
+  return WI_OK;
+}
+
+// Build workspace layout; with base == nullptr only the size is computed.
+int64_t carve_build(const wi::Geom& g, uint8_t* base, wi::BuildWs* w) {
+  const int64_t P = (int64_t)g.U * g.n_idx;
+  const int nsl = (g.seg_len + wi::KPP_SLICE - 1) / wi::KPP_SLICE;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    uint8_t* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  wi::BuildWs t;
+  t.D = reinterpret_cast<float*>(take(P * 4));
+  t.w[0] = reinterpret_cast<unsigned long long*>(take(P * 8));
+  t.w[1] = reinterpret_cast<unsigned long long*>(take(P * 8));
+  t.chosen = take(P);
+  t.kpp = reinterpret_cast<wi::KppPartial*>(
+      take((int64_t)g.U * g.n_seg * nsl * (int64_t)sizeof(wi::KppPartial)));
+  t.label = reinterpret_cast<int*>(take(P * 4));
+  t.members = reinterpret_cast<int*>(take(P * 4));
+  t.cl_off = reinterpret_cast<int*>(take((int64_t)g.U * g.C * 4));
+  t.amb = reinterpret_cast<int*>(take((P + 1) * 4));
+  t.seg_blocks = reinterpret_cast<int*>(take((int64_t)g.U * g.n_seg * 4));
+  t.seg_bbase = reinterpret_cast<int*>(take((int64_t)g.U * g.n_seg * 4));
+  t.unit_used = reinterpret_cast<int*>(take((int64_t)g.U * 4));
+  if (w) *w = t;
+  return off;
+}
+
+struct DecodeShape {
+  int Hq, G, K_r, K_e, P;
+  float scale;
+};
+
+wi_status make_decode(const wi::Geom& g, const wi_decode_desc* dd, DecodeShape* o) {
+  if (!dd) return fail(WI_E_INVALID, "decode desc is NULL");
+  if (dd->n_q_heads < 1 || dd->n_q_heads % g.H)
+    return fail(WI_E_UNSUPPORTED, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                dd->n_q_heads, g.H);
+  const int G = dd->n_q_heads / g.H;
+  if (G > wi::MAX_G) return fail(WI_E_UNSUPPORTED, "%d query heads per KV head > %d", G, wi::MAX_G);
+  if (dd->k_retrieve < 0 || dd->k_retrieve > g.C)
+    return fail(WI_E_INVALID, "k_retrieve %d outside [0, C=%d]", dd->k_retrieve, g.C);
+  if (dd->k_estimate < 0) return fail(WI_E_INVALID, "k_estimate %d < 0", dd->k_estimate);
+  if (!(dd->scale >= 0.f) || !std::isfinite(dd->scale))
+    return fail(WI_E_INVALID, "scale must be finite and >= 0");
+  o->Hq = dd->n_q_heads;
+  o->G = G;
+  o->K_r = dd->k_retrieve;
+  o->K_e = dd->k_estimate < g.C - dd->k_retrieve ? dd->k_estimate : g.C - dd->k_retrieve;
+  o->scale = dd->scale > 0.f ? dd->scale : 1.0f / std::sqrt((float)wi::D);
+  // chunks per unit: about 64 work items (tokens or estimation clusters) each
+  const double per_cluster = (double)g.n_idx / (double)g.C;
+  const double items = g.n_st + o->K_r * per_cluster + o->K_e;
+  int P = (int)std::ceil(items / 64.0);
+  if (P < 1) P = 1;
+  if (P > 1024) P = 1024;
+  o->P = P;
+  return WI_OK;
+}
+
+int64_t carve_decode(const wi::Geom& g, const DecodeShape& ds, uint8_t* base, wi::DecodeWs* w) {
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    uint8_t* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  wi::DecodeWs t;
+  t.key = reinterpret_cast<uint32_t*>(take((int64_t)g.U * g.C * 4));
+  t.S = reinterpret_cast<float*>(take((int64_t)g.U * g.C * ds.G * 4));
+  t.R = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_r * 4));
+  t.E = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_e * 4));
+  t.Rpre = reinterpret_cast<int*>(take((int64_t)g.U * (ds.K_r + 1) * 4));
+  t.rank = reinterpret_cast<int*>(take((int64_t)g.U * (ds.K_r + ds.K_e) * 4));
+  t.part = reinterpret_cast<float*>(take((int64_t)g.U * ds.P * ds.G * (2 + wi::D) * 4));
+  if (w) *w = t;
+  return off;
+}
+
+#define CHECK_PTR(p, name)                                              \
+  do {                                                                  \
+    if (!(p)) return fail(WI_E_INVALID, "%s is NULL", name);            \
+    if (!aligned16(p)) return fail(WI_E_INVALID, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define CHECK_HIP(expr, where)                 \
+  do {                                         \
+    hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+// Measurement hook state (per host thread).
+struct TimingRec {
+  int id;
+  hipEvent_t a, b;
+};
+thread_local bool t_on = false;
+thread_local std::vector<TimingRec> t_recs;
+thread_local std::vector<hipEvent_t> t_pool;
+thread_local int t_cur = -1;
+
+const char* const kNames[wi::K_COUNT] = {
+    "zero", "copy_init", "kpp_init", "kpp_weights", "kpp_round", "assign", "assign_fix",
+    "sort_update", "seg_scan", "layout", "score", "select", "attend", "combine", "rank",
+    "exec"};
+
+hipEvent_t take_event() {
+  if (!t_pool.empty()) {
+    hipEvent_t e = t_pool.back();
+    t_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace wi {
+void tmark_begin(KernelId id, hipStream_t s) {
+  if (!t_on) return;
+  TimingRec r{(int)id, take_event(), take_event()};
+  if (r.a) hipEventRecord(r.a, s);
+  t_recs.push_back(r);
+  t_cur = (int)t_recs.size() - 1;
+}
+void tmark_end(hipStream_t s) {
+  if (!t_on || t_cur < 0) return;
+  if (t_recs[t_cur].b) hipEventRecord(t_recs[t_cur].b, s);
+  t_cur = -1;
+}
+}  // namespace wi
+
+extern "C" {
+
+wi_status wi_timing_start(void) {
+  t_on = true;
+  t_recs.clear();
+  return WI_OK;
+}
+
+int32_t wi_timing_stop(int32_t max_records, int32_t* name_ids, float* ms) {
+  t_on = false;
+  int32_t n = (int32_t)t_recs.size();
+  int32_t rc = n;
+  for (int32_t i = 0; i < n; i++) {
+    TimingRec& r = t_recs[i];
+    float t = -1.f;
+    if (r.a && r.b) {
+      if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+        rc = -1;
+    }
+    if (i < max_records) {
+      if (name_ids) name_ids[i] = r.id;
+      if (ms) ms[i] = t;
+    }
+    if (r.a) t_pool.push_back(r.a);
+    if (r.b) t_pool.push_back(r.b);
+  }
+  t_recs.clear();
+  return rc;
+}
+
+const char* wi_kernel_name(int32_t id) {
+  return (id >= 0 && id < wi::K_COUNT) ? kNames[id] : "unknown";
+}
+
+
+const char* wi_status_str(wi_status s) {
+  switch (s) {
+    case WI_OK: return "WI_OK";
+    case WI_E_INVALID: return "WI_E_INVALID";
+    case WI_E_UNSUPPORTED: return "WI_E_UNSUPPORTED";
+    case WI_E_WORKSPACE: return "WI_E_WORKSPACE";
+    case WI_E_HIP: return "WI_E_HIP";
+  }
+  return "WI_E_UNKNOWN";
+}
+
+const char* wi_last_error(void) { return g_err; }
+
+wi_status wi_index_sizes(const wi_index_desc* desc, int64_t* n_segments, int64_t* n_clusters,
+                         int64_t* block_cap, size_t* workspace_bytes) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  if (n_segments) *n_segments = g.n_seg;
+  if (n_clusters) *n_clusters = g.C;
+  if (block_cap) *block_cap = g.cap;
+  if (workspace_bytes) *workspace_bytes = (size_t)carve_build(g, nullptr, nullptr);
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_build_index(const wi_index_desc* desc, const void* k, const void* v,
+                         const void* init_centroids, const wi_index_bufs* bufs, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  if (init_centroids && !aligned16(init_centroids))
+    return fail(WI_E_INVALID, "init_centroids is not 16-byte aligned");
+  if (!bufs) return fail(WI_E_INVALID, "bufs is NULL");
+  CHECK_PTR(bufs->centroids, "bufs->centroids");
+  CHECK_PTR(bufs->cluster_size, "bufs->cluster_size");
+  CHECK_PTR(bufs->value_sum, "bufs->value_sum");
+  CHECK_PTR(bufs->block_off, "bufs->block_off");
+  CHECK_PTR(bufs->k_blocks, "bufs->k_blocks");
+  CHECK_PTR(bufs->v_blocks, "bufs->v_blocks");
+  CHECK_PTR(bufs->slot_token, "bufs->slot_token");
+  CHECK_PTR(bufs->assign, "bufs->assign");
+  if (g.n_st > 0) {
+    CHECK_PTR(bufs->steady_k, "bufs->steady_k");
+    CHECK_PTR(bufs->steady_v, "bufs->steady_v");
+  }
+  const int64_t need = carve_build(g, nullptr, nullptr);
+  if (!ws || (int64_t)ws_bytes < need)
+    return fail(WI_E_WORKSPACE, "workspace %zu bytes < %lld required", ws_bytes, (long long)need);
+  if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
+  wi::BuildWs w;
+  carve_build(g, reinterpret_cast<uint8_t*>(ws), &w);
+
+  if (init_centroids)
+    CHECK_HIP(wi::launch_copy_init(g, init_centroids, bufs->centroids, stream), "copy init");
+  else
+    CHECK_HIP(wi::launch_kpp(g, k, bufs->centroids, w, stream), "k-means++");
+  const int iters = g.n_iters > 0 ? g.n_iters : 1;
+  for (int t = 0; t < iters; t++) {
+    CHECK_HIP(wi::launch_assign(g, k, bufs->centroids, w, stream), "assign");
+    CHECK_HIP(wi::launch_sort_update(g, k, bufs->centroids, bufs->cluster_size, w,
+                                     g.n_iters > 0, stream),
+              "update");
+  }
+  CHECK_HIP(wi::launch_layout(g, k, v, *bufs, w, stream), "layout");
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_decode_sizes(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                          size_t* workspace_bytes) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  DecodeShape ds;
+  st = make_decode(g, ddesc, &ds);
+  if (st != WI_OK) return st;
+  if (workspace_bytes) *workspace_bytes = (size_t)carve_decode(g, ds, nullptr, nullptr);
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_decode_attention(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                              const wi_index_bufs* bufs, const void* q, float* out,
+                              int32_t* sel_ids, int32_t* exec_tokens, int32_t* n_exec,
+                              int64_t exec_cap, void* ws, size_t ws_bytes, hipStream_t stream) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  DecodeShape ds;
+  st = make_decode(g, ddesc, &ds);
+  if (st != WI_OK) return st;
+  if (!bufs) return fail(WI_E_INVALID, "bufs is NULL");
+  CHECK_PTR(bufs->centroids, "bufs->centroids");
+  CHECK_PTR(bufs->cluster_size, "bufs->cluster_size");
+  CHECK_PTR(bufs->value_sum, "bufs->value_sum");
+  CHECK_PTR(bufs->block_off, "bufs->block_off");
+  CHECK_PTR(bufs->k_blocks, "bufs->k_blocks");
+  CHECK_PTR(bufs->v_blocks, "bufs->v_blocks");
+  if (g.n_st > 0) {
+    CHECK_PTR(bufs->steady_k, "bufs->steady_k");
+    CHECK_PTR(bufs->steady_v, "bufs->steady_v");
+  }
+  CHECK_PTR(q, "q");
+  CHECK_PTR(out, "out");
+  if (sel_ids && !aligned16(sel_ids)) return fail(WI_E_INVALID, "sel_ids is not 16-byte aligned");
+  if (n_exec && !aligned16(n_exec)) return fail(WI_E_INVALID, "n_exec is not 16-byte aligned");
+  if (exec_tokens) {
+    if (!aligned16(exec_tokens)) return fail(WI_E_INVALID, "exec_tokens is not 16-byte aligned");
+    if (exec_cap < 0) return fail(WI_E_INVALID, "exec_cap < 0");
+    CHECK_PTR(bufs->slot_token, "bufs->slot_token");
+  }
+  const int64_t need = carve_decode(g, ds, nullptr, nullptr);
+  if (!ws || (int64_t)ws_bytes < need)
+    return fail(WI_E_WORKSPACE, "workspace %zu bytes < %lld required", ws_bytes, (long long)need);
+  if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
+  wi::DecodeWs w;
+  carve_decode(g, ds, reinterpret_cast<uint8_t*>(ws), &w);
+  wi::DecodeArgs a{&g, ds.Hq, ds.G, ds.K_r, ds.K_e, ds.P, ds.scale, bufs->cluster_size};
+
+  CHECK_HIP(wi::launch_score(a, bufs->centroids, q, w, stream), "score");
+  CHECK_HIP(wi::launch_select(a, w, stream), "select");
+  CHECK_HIP(wi::launch_attend(a, *bufs, q, out, w, stream), "attend");
+  if (sel_ids || exec_tokens || n_exec)
+    CHECK_HIP(wi::launch_debug_outputs(a, *bufs, w, sel_ids, exec_tokens, n_exec, exec_cap,
+                                       stream),
+              "debug outputs");
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+}  // extern "C"

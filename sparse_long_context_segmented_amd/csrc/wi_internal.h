@@ -1,0 +1,199 @@
+// Internal declarations shared by the HIP translation units of libwi.so.
+// gfx950 only: wave64, MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/wi.h"
+
+namespace wi {
+
+constexpr int D = 128;          // head_dim
+constexpr int MAX_G = 16;       // query heads per KV head
+constexpr int MAX_K = 512;      // clusters per segment
+constexpr int MAX_SEG = 8192;   // tokens per segment
+
+// ---------------------------------------------------------------------------
+// Geometry of one call, computed on the host from the descriptor.
+struct Geom {
+  int dtype;        // WI_F32 / WI_BF16
+  int B, H, U;      // batch, KV heads, units
+  int64_t N;        // context tokens
+  int n_sink, n_local, n_st;
+  int64_t n_idx;    // indexed tokens per unit
+  int seg_len, kk;  // segment length, clusters per full segment
+  int n_seg;        // segments per unit
+  int C;            // clusters per unit
+  int T;            // tokens per 2 KB block
+  int64_t cap;      // block capacity per unit
+  int64_t sb, sh, st;  // K/V element strides
+  uint64_t seed;
+  uint32_t layer;
+  int n_iters;
+  int cmax;         // max clusters of any segment = min(kk, seg_len, n_idx)
+};
+
+// Segment s of a unit: first indexed position, length, cluster count/base.
+__host__ __device__ inline int64_t seg_first(const Geom& g, int s) {
+  return (int64_t)g.n_sink + (int64_t)s * g.seg_len;
+}
+__host__ __device__ inline int seg_n(const Geom& g, int s) {
+  int64_t left = g.n_idx - (int64_t)s * g.seg_len;
+  return (int)(left < g.seg_len ? left : g.seg_len);
+}
+__host__ __device__ inline int seg_c(const Geom& g, int s) {
+  int n = seg_n(g, s);
+  return n < g.kk ? n : g.kk;
+}
+__host__ __device__ inline int seg_cbase(const Geom& g, int s) {
+  int full = g.seg_len < g.kk ? g.seg_len : g.kk;  // clusters of a full segment
+  return s * full;
+}
+
+// ---------------------------------------------------------------------------
+// Build workspace (device pointers carved from the caller's buffer).
+struct KppPartial {
+  unsigned long long sum[2];  // per parity: sum of weights of the slice
+  int minun[2];               // per parity: smallest unchosen local index
+  float maxd;                 // max distance after the first pick
+  int pad;
+};
+
+struct BuildWs {
+  float* D;                    // [U*n_idx] k-means++ distances
+  unsigned long long* w[2];    // [U*n_idx] k-means++ weights, by parity
+  unsigned char* chosen;       // [U*n_idx]
+  KppPartial* kpp;             // [U*n_seg*kpp_slices]
+  int* label;                  // [U*n_idx] local cluster index per point
+  int* members;                // [U*n_idx] local token index, cluster order
+  int* cl_off;                 // [U*C] first member of each cluster (segment-local)
+  int* amb;                    // [1 + U*n_idx] ambiguous-point count + list
+  int* seg_blocks;             // [U*n_seg] blocks used by each segment
+  int* seg_bbase;              // [U*n_seg] first block of each segment
+  int* unit_used;              // [U] blocks used by each unit
+};
+constexpr int KPP_SLICE = 256;  // points per k-means++ workgroup
+
+// Decode workspace.
+struct DecodeWs {
+  uint32_t* key;     // [U*C] order-preserving ranking keys
+  float* S;          // [U*C*G] scaled per-head centroid logits
+  int* R;            // [U*K_r] retrieval clusters, ascending id
+  int* E;            // [U*K_e] estimation clusters, ascending id
+  int* Rpre;         // [U*(K_r+1)] prefix sums of R cluster sizes
+  int* rank;         // [U*(K_r+K_e)] selected ids in rank order (debug path)
+  float* part;       // [U*P*G*(2+128)] chunk partials (m, l, acc)
+};
+
+// ---------------------------------------------------------------------------
+// Device helpers.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// SplitMix64 output finaliser (Steele, Lea and Flood, OOPSLA 2014).
+__host__ __device__ inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+// Counter-based draw for (seed, b, layer, h, segment, round).
+__host__ __device__ inline uint64_t draw_key(uint64_t seed, uint64_t b, uint64_t l,
+                                             uint64_t h, uint64_t s, uint64_t r) {
+  const uint64_t G = 0x9E3779B97F4A7C15ull;
+  uint64_t k = mix64(seed + G);
+  k = mix64(k ^ (b + G));
+  k = mix64(k ^ (l + G));
+  k = mix64(k ^ (h + G));
+  k = mix64(k ^ (s + G));
+  return mix64(k ^ (r + G));
+}
+// floor((key >> 11) * m / 2^53), m < 2^63.
+__device__ __forceinline__ uint64_t scale53(uint64_t key, uint64_t m) {
+  uint64_t r = key >> 11;
+  uint64_t lo = r * m;
+  uint64_t hi = __umul64hi(r, m);
+  return (hi << 11) | (lo >> 53);
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Wave-wide reductions (wave64).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Measurement hook (see wi_timing_start): no-ops unless enabled on this
+// thread. Kernel name ids index a fixed table.
+enum KernelId {
+  K_ZERO, K_COPY, K_KPP_INIT, K_KPP_WEIGHTS, K_KPP_ROUND, K_ASSIGN, K_ASSIGN_FIX,
+  K_SORT_UPDATE, K_SEG_SCAN, K_LAYOUT, K_SCORE, K_SELECT, K_ATTEND, K_COMBINE, K_RANK,
+  K_EXEC, K_COUNT
+};
+void tmark_begin(KernelId id, hipStream_t s);
+void tmark_end(hipStream_t s);
+
+// Launch a kernel bracketed by the measurement hook.
+#define WI_LAUNCH(ID, KERNEL, GRID, BLOCK, LDS, STREAM, ...)                \
+  do {                                                                      \
+    ::wi::tmark_begin(ID, STREAM);                                          \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);      \
+    ::wi::tmark_end(STREAM);                                                \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// Launchers (host functions, one per kernel family). Each returns the HIP
+// status of its launches.
+hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t s);
+
+hipError_t launch_kpp(const Geom& g, const void* K, void* centroids,
+                      const BuildWs& ws, hipStream_t s);
+hipError_t launch_copy_init(const Geom& g, const void* init, void* centroids,
+                            hipStream_t s);
+hipError_t launch_assign(const Geom& g, const void* K, const void* centroids,
+                         const BuildWs& ws, hipStream_t s);
+hipError_t launch_sort_update(const Geom& g, const void* K, void* centroids,
+                              int32_t* cluster_size, const BuildWs& ws,
+                              bool do_update, hipStream_t s);
+hipError_t launch_layout(const Geom& g, const void* K, const void* V,
+                         const wi_index_bufs& b, const BuildWs& ws,
+                         hipStream_t s);
+
+struct DecodeArgs {
+  const Geom* g;
+  int Hq, G, K_r, K_e, P;
+  float scale;
+  const int32_t* sizes;  // cluster sizes [U][C]
+};
+hipError_t launch_score(const DecodeArgs& a, const void* centroids, const void* q,
+                        const DecodeWs& ws, hipStream_t s);
+hipError_t launch_select(const DecodeArgs& a, const DecodeWs& ws, hipStream_t s);
+hipError_t launch_attend(const DecodeArgs& a, const wi_index_bufs& b, const void* q,
+                         float* out, const DecodeWs& ws, hipStream_t s);
+hipError_t launch_debug_outputs(const DecodeArgs& a, const wi_index_bufs& b,
+                                const DecodeWs& ws, int32_t* sel_ids,
+                                int32_t* exec_tokens, int32_t* n_exec,
+                                int64_t exec_cap, hipStream_t s);
+
+}  // namespace wi

@@ -1,0 +1,228 @@
+"""ctypes binding of libwi.so (C ABI in include/wi.h).
+
+Argument marshalling only: every step of the build and the decode runs in the
+library's HIP kernels. torch provides device memory and the stream. The
+library must be built (``python -m sparse_long_context_segmented_amd._build``
+or ``__graft_entry__.build()``); loading fails loudly if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwi.so")
+
+WI_F32, WI_BF16 = 0, 1
+STATUS = {0: "WI_OK", 1: "WI_E_INVALID", 2: "WI_E_UNSUPPORTED", 3: "WI_E_WORKSPACE",
+          4: "WI_E_HIP"}
+EXPORTS = ("wi_index_sizes", "wi_build_index", "wi_decode_sizes", "wi_decode_attention",
+           "wi_status_str", "wi_last_error", "wi_timing_start", "wi_timing_stop",
+           "wi_kernel_name")
+
+
+class WIError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class IndexDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_ctx", ctypes.c_int64), ("seg_len", ctypes.c_int32),
+                ("clusters_per_seg", ctypes.c_int32), ("n_sink", ctypes.c_int32),
+                ("n_local", ctypes.c_int32), ("n_iters", ctypes.c_int32),
+                ("seed", ctypes.c_uint64), ("layer_id", ctypes.c_uint32),
+                ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
+                ("kv_stride_t", ctypes.c_int64)]
+
+
+class IndexBufs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "centroids", "cluster_size", "value_sum", "block_off", "k_blocks", "v_blocks",
+        "slot_token", "steady_k", "steady_v", "assign")]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("k_retrieve", ctypes.c_int32),
+                ("k_estimate", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libwi.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_long_context_segmented_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.wi_index_sizes.argtypes = [P, P, P, P, P]
+        L.wi_index_sizes.restype = ctypes.c_int
+        L.wi_build_index.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.wi_build_index.restype = ctypes.c_int
+        L.wi_decode_sizes.argtypes = [P, P, P]
+        L.wi_decode_sizes.restype = ctypes.c_int
+        L.wi_decode_attention.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int64, P,
+                                          ctypes.c_size_t, P]
+        L.wi_decode_attention.restype = ctypes.c_int
+        L.wi_status_str.argtypes = [ctypes.c_int]
+        L.wi_status_str.restype = ctypes.c_char_p
+        L.wi_last_error.argtypes = []
+        L.wi_last_error.restype = ctypes.c_char_p
+        L.wi_timing_start.argtypes = []
+        L.wi_timing_start.restype = ctypes.c_int
+        L.wi_timing_stop.argtypes = [ctypes.c_int32, P, P]
+        L.wi_timing_stop.restype = ctypes.c_int32
+        L.wi_kernel_name.argtypes = [ctypes.c_int32]
+        L.wi_kernel_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise WIError(rc, lib().wi_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_desc(dtype: str, batch: int, n_kv_heads: int, n_ctx: int, seg_len: int = 8192,
+              clusters_per_seg: int = 512, n_sink: int = 4, n_local: int = 64,
+              n_iters: int = 10, seed: int = 0, layer_id: int = 0,
+              strides=None) -> IndexDesc:
+    """Descriptor; strides default to a contiguous [B, H, N, 128] K/V."""
+    if strides is None:
+        strides = (n_kv_heads * n_ctx * 128, n_ctx * 128, 128)
+    return IndexDesc(WI_F32 if dtype == "f32" else WI_BF16, batch, n_kv_heads, 128, n_ctx,
+                     seg_len, clusters_per_seg, n_sink, n_local, n_iters, seed, layer_id,
+                     *strides)
+
+
+def index_sizes(desc: IndexDesc):
+    ns, c, cap = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    ws = ctypes.c_size_t()
+    _check(lib().wi_index_sizes(ctypes.byref(desc), ctypes.byref(ns), ctypes.byref(c),
+                                ctypes.byref(cap), ctypes.byref(ws)))
+    return ns.value, c.value, cap.value, ws.value
+
+
+def torch_dtype(desc: IndexDesc):
+    return torch.float32 if desc.dtype == WI_F32 else torch.bfloat16
+
+
+@dataclass
+class Index:
+    """Device tensors of a built index (all owned by torch)."""
+    desc: IndexDesc
+    centroids: torch.Tensor
+    cluster_size: torch.Tensor
+    value_sum: torch.Tensor
+    block_off: torch.Tensor
+    k_blocks: torch.Tensor
+    v_blocks: torch.Tensor
+    slot_token: torch.Tensor
+    steady_k: torch.Tensor
+    steady_v: torch.Tensor
+    assign: torch.Tensor
+
+    def bufs(self) -> IndexBufs:
+        return IndexBufs(*[_ptr(getattr(self, n)) for n, _ in IndexBufs._fields_])
+
+
+def alloc_index(desc: IndexDesc, device="cuda") -> Index:
+    ns, C, cap, _ = index_sizes(desc)
+    U = desc.batch * desc.n_kv_heads
+    T = 2048 // (128 * (4 if desc.dtype == WI_F32 else 2))
+    dt = torch_dtype(desc)
+    n_idx = desc.n_ctx - desc.n_sink - desc.n_local
+    n_st = desc.n_sink + desc.n_local
+    e = lambda *s, dtype=dt: torch.empty(*s, dtype=dtype, device=device)  # noqa: E731
+    return Index(desc, e(U, C, 128), e(U, C, dtype=torch.int32), e(U, C, 128, dtype=torch.float32),
+                 e(U, C + 1, dtype=torch.int32), e(U, cap * T, 128), e(U, cap * T, 128),
+                 e(U, cap * T, dtype=torch.int32), e(U, max(n_st, 1), 128),
+                 e(U, max(n_st, 1), 128), e(U, n_idx, dtype=torch.int32))
+
+
+def index_from_host(desc: IndexDesc, arrays: dict, device="cuda") -> Index:
+    """Upload an index given as host arrays (keys as in the oracle's output)."""
+    dt = torch_dtype(desc)
+    t = lambda a, dtype=dt: torch.as_tensor(a).to(device=device, dtype=dtype).contiguous()  # noqa: E731
+    return Index(desc, t(arrays["centroids"]), t(arrays["sizes"], torch.int32),
+                 t(arrays["vsum"], torch.float32), t(arrays["block_off"], torch.int32),
+                 t(arrays["kblk"]), t(arrays["vblk"]), t(arrays["slot_token"], torch.int32),
+                 t(arrays["steady_k"]), t(arrays["steady_v"]), t(arrays["assign"], torch.int32))
+
+
+def build_index(desc: IndexDesc, k: torch.Tensor, v: torch.Tensor,
+                init: torch.Tensor | None = None, index: Index | None = None,
+                ws: torch.Tensor | None = None, stream=None) -> Index:
+    """Run wi_build_index on device tensors k, v laid out as desc's strides say."""
+    _, _, _, wsb = index_sizes(desc)
+    if index is None:
+        index = alloc_index(desc, k.device)
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=k.device)
+    bufs = index.bufs()
+    _check(lib().wi_build_index(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(init),
+                                ctypes.byref(bufs), _ptr(ws), ws.numel(), _stream(stream)))
+    return index
+
+
+def decode_sizes(desc: IndexDesc, ddesc: DecodeDesc) -> int:
+    ws = ctypes.c_size_t()
+    _check(lib().wi_decode_sizes(ctypes.byref(desc), ctypes.byref(ddesc), ctypes.byref(ws)))
+    return ws.value
+
+
+def decode_attention(index: Index, ddesc: DecodeDesc, q: torch.Tensor,
+                     out: torch.Tensor | None = None, sel_ids: torch.Tensor | None = None,
+                     exec_tokens: torch.Tensor | None = None,
+                     n_exec: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """Run wi_decode_attention; returns out [B, Hq, 128] float32."""
+    desc = index.desc
+    wsb = decode_sizes(desc, ddesc)
+    if out is None:
+        out = torch.empty(desc.batch, ddesc.n_q_heads, 128, dtype=torch.float32, device=q.device)
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    bufs = index.bufs()
+    exec_cap = 0 if exec_tokens is None else exec_tokens.shape[-1]
+    _check(lib().wi_decode_attention(ctypes.byref(desc), ctypes.byref(ddesc), ctypes.byref(bufs),
+                                     _ptr(q), _ptr(out), _ptr(sel_ids), _ptr(exec_tokens),
+                                     _ptr(n_exec), exec_cap, _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+    return out
+
+
+def timing_start():
+    """Bracket every following kernel launch of this thread with HIP events."""
+    _check(lib().wi_timing_start())
+
+
+def timing_stop(max_records: int = 1 << 16):
+    """Stop timing; returns a list of (kernel name, milliseconds) in issue order."""
+    import numpy as np
+    ids = np.zeros(max_records, np.int32)
+    ms = np.zeros(max_records, np.float32)
+    n = lib().wi_timing_stop(max_records, ids.ctypes.data, ms.ctypes.data)
+    if n < 0:
+        raise WIError(4, "timing events failed")
+    n = min(n, max_records)
+    return [(lib().wi_kernel_name(int(i)).decode(), float(t)) for i, t in zip(ids[:n], ms[:n])]

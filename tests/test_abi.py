@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/wi.h declares, derives the same sizes as the oracle, and rejects every
+invalid call on the host before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from sparse_long_context_segmented_amd import wi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(wi.LIB_PATH):
+        from sparse_long_context_segmented_amd import _build
+        _build.build()
+    return wi.lib()
+
+
+def _declared():
+    hdr = open(os.path.join(ROOT, "include", "wi.h")).read()
+    return sorted(set(re.findall(r"\b(wi_[a-z_]+)\s*\(", hdr)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(wi.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", wi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in names:
+        assert n in exported, n
+        assert getattr(L, n) is not None
+
+
+def test_status_strings(L):
+    for code, name in wi.STATUS.items():
+        assert L.wi_status_str(code).decode() == name
+
+
+@pytest.mark.parametrize("dtype,B,H,N,seg,k", [
+    ("bf16", 1, 8, 131072, 8192, 512), ("f32", 1, 1, 8192, 8192, 512),
+    ("bf16", 4, 4, 262144, 8192, 512), ("bf16", 2, 3, 68 + 3 * 96 + 37, 96, 12),
+    ("bf16", 1, 1, 69, 8192, 512), ("f32", 1, 2, 68 + 40, 16, 16)])
+def test_sizes_match_oracle(L, dtype, B, H, N, seg, k):
+    d = wi.make_desc(dtype, B, H, N, seg_len=seg, clusters_per_seg=k)
+    ns, C, cap, ws = wi.index_sizes(d)
+    ons, oC, ocap, T = oracle.sizes(oracle.make_desc(dtype, B, H, N, seg_len=seg,
+                                                     clusters_per_seg=k))
+    assert (ns, C, cap) == (ons, oC, ocap)
+    assert ws > 0
+
+
+def test_sizes_of_named_workloads(L):
+    # segments, clusters and block capacity per unit of the five shapes
+    exp = {131072: (16, 8192, 23543), 8192: (1, 512, 2415), 262144: (32, 16384, 47095),
+           1048576: (128, 65536, 188407)}
+    for n, (ns, c, cap) in exp.items():
+        dt = "f32" if n == 8192 else "bf16"
+        assert wi.index_sizes(wi.make_desc(dt, 1, 1, n))[:3] == (ns, c, cap)
+
+
+def _bad_build(L, desc, ptrs=None, ws_bytes=1 << 40):
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+    p = dict(k=fake, v=fake, init=None, ws=fake)
+    if ptrs:
+        p.update(ptrs)
+    bufs = wi.IndexBufs(*([0x100000] * 10))
+    return L.wi_build_index(ctypes.byref(desc), p["k"], p["v"], p["init"], ctypes.byref(bufs),
+                            p["ws"], ws_bytes, None), bufs
+
+
+def test_build_rejects_bad_descriptors(L):
+    def expect(code, **kw):
+        d = wi.make_desc("bf16", 1, 2, 4096, seg_len=1024, clusters_per_seg=64)
+        for k_, v_ in kw.items():
+            setattr(d, k_, v_)
+        rc, _ = _bad_build(L, d)
+        assert rc == code, (kw, rc, L.wi_last_error())
+        assert L.wi_last_error().decode()
+    expect(2, head_dim=64)
+    expect(2, dtype=7)
+    expect(1, batch=0)
+    expect(1, n_kv_heads=0)
+    expect(1, n_ctx=68)
+    expect(1, n_sink=-1)
+    expect(1, seg_len=0)
+    expect(1, seg_len=8193)
+    expect(1, clusters_per_seg=0)
+    expect(1, clusters_per_seg=513)
+    expect(1, n_iters=-1)
+    expect(1, kv_stride_t=0)
+    expect(1, kv_stride_t=129)
+    expect(1, kv_stride_h=-8)
+
+
+def test_build_rejects_bad_pointers_and_workspace(L):
+    d = wi.make_desc("bf16", 1, 2, 4096, seg_len=1024, clusters_per_seg=64)
+    rc, _ = _bad_build(L, d, dict(k=None))
+    assert rc == 1 and b"k is NULL" in L.wi_last_error()
+    rc, _ = _bad_build(L, d, dict(v=ctypes.c_void_p(0x100004)))
+    assert rc == 1 and b"aligned" in L.wi_last_error()
+    rc, _ = _bad_build(L, d, dict(init=ctypes.c_void_p(0x100008)))
+    assert rc == 1
+    need = wi.index_sizes(d)[3]
+    rc, _ = _bad_build(L, d, ws_bytes=need - 1)
+    assert rc == 3
+    rc, _ = _bad_build(L, d, dict(ws=None), ws_bytes=need)
+    assert rc == 3
+    bufs = wi.IndexBufs(*([0x100000] * 10))
+    bufs.centroids = None
+    fake = ctypes.c_void_p(0x100000)
+    rc = L.wi_build_index(ctypes.byref(d), fake, fake, None, ctypes.byref(bufs), fake, need, None)
+    assert rc == 1 and b"centroids" in L.wi_last_error()
+    rc = L.wi_build_index(ctypes.byref(d), fake, fake, None, None, fake, need, None)
+    assert rc == 1
+    rc = L.wi_build_index(None, fake, fake, None, ctypes.byref(bufs), fake, need, None)
+    assert rc == 1
+
+
+def _decode(L, desc, dd, **kw):
+    fake = ctypes.c_void_p(0x100000)
+    bufs = wi.IndexBufs(*([0x100000] * 10))
+    if "bufs" in kw:
+        bufs = kw.pop("bufs")
+    args = dict(q=fake, out=fake, sel=None, exe=None, nexe=None, cap=0, ws=fake,
+                ws_bytes=1 << 40)
+    args.update(kw)
+    return L.wi_decode_attention(ctypes.byref(desc), ctypes.byref(dd), ctypes.byref(bufs),
+                                 args["q"], args["out"], args["sel"], args["exe"],
+                                 args["nexe"], args["cap"], args["ws"], args["ws_bytes"], None)
+
+
+def test_decode_rejects_invalid_calls(L):
+    d = wi.make_desc("bf16", 2, 4, 4096, seg_len=1024, clusters_per_seg=64)
+    C = wi.index_sizes(d)[1]
+    assert _decode(L, d, wi.DecodeDesc(6, 4, 10, 0.0)) == 2       # Hq % Hkv
+    assert _decode(L, d, wi.DecodeDesc(4 * 17, 4, 10, 0.0)) == 2  # G > 16
+    assert _decode(L, d, wi.DecodeDesc(16, C + 1, 10, 0.0)) == 1  # K_r > C
+    assert _decode(L, d, wi.DecodeDesc(16, -1, 10, 0.0)) == 1
+    assert _decode(L, d, wi.DecodeDesc(16, 4, -1, 0.0)) == 1
+    assert _decode(L, d, wi.DecodeDesc(16, 4, 10, -1.0)) == 1
+    assert _decode(L, d, wi.DecodeDesc(16, 4, 10, float("nan"))) == 1
+    assert _decode(L, d, wi.DecodeDesc(16, 4, 10, 0.0), q=None) == 1
+    assert _decode(L, d, wi.DecodeDesc(16, 4, 10, 0.0), out=ctypes.c_void_p(0x100002)) == 1
+    need = wi.decode_sizes(d, wi.DecodeDesc(16, 4, 10, 0.0))
+    assert _decode(L, d, wi.DecodeDesc(16, 4, 10, 0.0), ws_bytes=need - 1) == 3
+    bufs = wi.IndexBufs(*([0x100000] * 10))
+    bufs.slot_token = None
+    assert _decode(L, d, wi.DecodeDesc(16, 4, 10, 0.0), bufs=bufs,
+                   exe=ctypes.c_void_p(0x100000), cap=10) == 1
+    d.head_dim = 96
+    assert _decode(L, d, wi.DecodeDesc(16, 4, 10, 0.0)) == 2
+
+
+def test_decode_sizes_grow_with_budget(L):
+    d = wi.make_desc("bf16", 1, 8, 131072)
+    a = wi.decode_sizes(d, wi.DecodeDesc(32, 147, 1884, 0.0))
+    b = wi.decode_sizes(d, wi.DecodeDesc(32, 1000, 4000, 0.0))
+    assert b > a > 8 * 8192 * 4
+    # K_e is clamped to C - K_r
+    assert wi.decode_sizes(d, wi.DecodeDesc(32, 8192, 5000, 0.0)) > 0

@@ -354,7 +354,8 @@ def test_select_matches_lexsort(orc):
     for u in range(d.batch * d.n_kv_heads):
         b, h = divmod(u, d.n_kv_heads)
         g = (q[b, h * G:(h + 1) * G].astype(np.float64) @ idx["centroids"][u].astype(np.float64).T).sum(0)
-        order = np.lexsort((np.arange(C), -g))
+        # ranking key: the float64 group score rounded to float32
+        order = np.lexsort((np.arange(C), -g.astype(np.float32).astype(np.float64)))
         assert np.array_equal(res["sel"][u], order[:14])
         assert np.allclose(res["gkey"][u], g, rtol=1e-12, atol=1e-12)
 
