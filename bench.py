@@ -165,7 +165,8 @@ def main():
     b_out = U * G * 128 * 4
     step_bytes = b_score + b_attend + b_out
     per_kernel = {"score": b_score, "attend": b_attend, "combine": b_out, "select": 0}
-    dom = max(avg, key=lambda k: avg[k])
+    # the dominant kernel among those that move the method's HBM bytes
+    dom = max((k for k in avg if per_kernel.get(k, 0) > 0), key=lambda k: avg[k])
     dom_bytes = per_kernel.get(dom, 0)
     achieved = dom_bytes / (avg[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),

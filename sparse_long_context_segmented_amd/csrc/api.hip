@@ -123,6 +123,7 @@ wi_status make_decode(const wi::Geom& g, const wi_decode_desc* dd, DecodeShape* 
                 dd->n_q_heads, g.H);
   const int G = dd->n_q_heads / g.H;
   if (G > wi::MAX_G) return fail(WI_E_UNSUPPORTED, "%d query heads per KV head > %d", G, wi::MAX_G);
+  if (g.C > 65536) return fail(WI_E_UNSUPPORTED, "%d clusters per unit > 65536", g.C);
   if (dd->k_retrieve < 0 || dd->k_retrieve > g.C)
     return fail(WI_E_INVALID, "k_retrieve %d outside [0, C=%d]", dd->k_retrieve, g.C);
   if (dd->k_estimate < 0) return fail(WI_E_INVALID, "k_estimate %d < 0", dd->k_estimate);
@@ -137,6 +138,10 @@ wi_status make_decode(const wi::Geom& g, const wi_decode_desc* dd, DecodeShape* 
   const double per_cluster = (double)g.n_idx / (double)g.C;
   const double items = g.n_st + o->K_r * per_cluster + o->K_e;
   int P = (int)std::ceil(items / 64.0);
+  // keep the attention grid within one resident wave of workgroups when
+  // it would otherwise spill into a short second one
+  const int resident = 512;  // 2 workgroups of the attention kernel per CU
+  if ((int64_t)g.U * P > resident) P = resident / g.U;
   if (P < 1) P = 1;
   if (P > 1024) P = 1024;
   o->P = P;
@@ -152,10 +157,14 @@ int64_t carve_decode(const wi::Geom& g, const DecodeShape& ds, uint8_t* base, wi
   };
   wi::DecodeWs t;
   t.key = reinterpret_cast<uint32_t*>(take((int64_t)g.U * g.C * 4));
-  t.S = reinterpret_cast<float*>(take((int64_t)g.U * g.C * ds.G * 4));
+  const int GS = ds.G <= 4 ? 4 : (ds.G <= 8 ? 8 : 16);  // padded heads per S row
+  t.S = reinterpret_cast<float*>(take((int64_t)g.U * g.C * GS * 4 + 64));
   t.R = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_r * 4));
-  t.E = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_e * 4));
+  t.Rblk = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_r * 4));
   t.Rpre = reinterpret_cast<int*>(take((int64_t)g.U * (ds.K_r + 1) * 4));
+  t.E = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_e * 4));
+  t.Esz = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_e * 4));
+  t.rowtab = reinterpret_cast<int*>(take((int64_t)g.U * g.n_idx * 4));
   t.rank = reinterpret_cast<int*>(take((int64_t)g.U * (ds.K_r + ds.K_e) * 4));
   t.part = reinterpret_cast<float*>(take((int64_t)g.U * ds.P * ds.G * (2 + wi::D) * 4));
   if (w) *w = t;
@@ -376,7 +385,7 @@ wi_status wi_decode_attention(const wi_index_desc* desc, const wi_decode_desc* d
   wi::DecodeArgs a{&g, ds.Hq, ds.G, ds.K_r, ds.K_e, ds.P, ds.scale, bufs->cluster_size};
 
   CHECK_HIP(wi::launch_score(a, bufs->centroids, q, w, stream), "score");
-  CHECK_HIP(wi::launch_select(a, w, stream), "select");
+  CHECK_HIP(wi::launch_select(a, *bufs, w, stream), "select");
   CHECK_HIP(wi::launch_attend(a, *bufs, q, out, w, stream), "attend");
   if (sel_ids || exec_tokens || n_exec)
     CHECK_HIP(wi::launch_debug_outputs(a, *bufs, w, sel_ids, exec_tokens, n_exec, exec_cap,

@@ -9,7 +9,8 @@
 // 256-byte rows per load instruction. The per-head dot products are reduced
 // across the 16 lanes with a fixed butterfly, so results are deterministic.
 //
-// Outputs per cluster c:  S[c][h] = scale * <q_h, mu_c>  (fp32, per head)
+// Outputs per cluster c:  S[c][h] = scale * <q_h, mu_c>  (fp32, per head; rows
+//                                    padded to GM = 4, 8 or 16 heads)
 //                         key[c]  = order-preserving bits of sum_h <q_h, mu_c>
 #include "wi_internal.h"
 
@@ -18,7 +19,6 @@ namespace {
 
 constexpr int SCORE_THREADS = 256;
 constexpr int GROUPS = SCORE_THREADS / 16;  // rows in flight per step
-constexpr int UNROLL = 4;                   // rows per group per step
 
 template <int DT>
 __device__ __forceinline__ void load_row8(const void* base, int64_t row, int j, float x[8]) {
@@ -44,64 +44,82 @@ __device__ __forceinline__ void load_row8(const void* base, int64_t row, int j, 
 // fp32) products are exact in float64 and on gfx950 a float64 FMA issues at
 // the float32 rate, so the group score is exact up to the final rounding to
 // float32 that the ranking is taken in.
+//
+// Latency: the whole score pass moves a few tens of MB, so every lane issues
+// all of its row loads (ROWS per 16-lane group, one 16-byte load each) before
+// any arithmetic; a workgroup covers GROUPS * ROWS rows.
+constexpr int ROWS = 4;
+
+template <int DT>
+__device__ __forceinline__ void raw_row(const void* base, int64_t row, int j, uint4 r[2]) {
+  if constexpr (DT == WI_BF16) {
+    r[0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + row * D + 8 * j);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + row * D + 8 * j);
+    r[0] = p[0];
+    r[1] = p[1];
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack8(const uint4 r[2], double xd[8]) {
+  if constexpr (DT == WI_BF16) {
+    const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      xd[2 * t] = (double)__uint_as_float(w[t] << 16);
+      xd[2 * t + 1] = (double)__uint_as_float(w[t] & 0xFFFF0000u);
+    }
+  } else {
+    const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+    for (int t = 0; t < 8; t++) xd[t] = (double)__uint_as_float(w[t]);
+  }
+}
+
 template <int DT, int GM>
 __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
     const void* __restrict__ cent, const void* __restrict__ q, int C, int G, int H,
-    int Hq, int cpb, float scale, uint32_t* __restrict__ key, float* __restrict__ S) {
+    int Hq, float scale, uint32_t* __restrict__ key, float* __restrict__ S) {
   const int u = blockIdx.y;
   const int b = u / H, h = u % H;
   const int tid = threadIdx.x;
   const int grp = tid >> 4, j = tid & 15;
-
-  double qv[GM][8];
-#pragma unroll
-  for (int g = 0; g < GM; g++) {
-    float t8[8];
-    if (g < G) {
-      load_row8<DT>(q, (int64_t)b * Hq + (int64_t)h * G + g, j, t8);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 8; t++) t8[t] = 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < 8; t++) qv[g][t] = (double)t8[t];
-  }
-
-  const int c0 = blockIdx.x * cpb;
-  const int c1 = min(C, c0 + cpb);
+  const int c0 = blockIdx.x * (GROUPS * ROWS);
   const int64_t rowbase = (int64_t)u * C;
-  for (int cb = c0 + grp; cb < c1; cb += GROUPS * UNROLL) {
-    float x[UNROLL][8];
+
+  // issue the row loads first
+  uint4 raw[ROWS][2];
 #pragma unroll
-    for (int r = 0; r < UNROLL; r++) {
-      const int c = cb + r * GROUPS;
-      if (c < c1) load_row8<DT>(cent, rowbase + c, j, x[r]);
-    }
+  for (int r = 0; r < ROWS; r++) {
+    const int c = c0 + r * GROUPS + grp;
+    if (c < C) raw_row<DT>(cent, rowbase + c, j, raw[r]);
+  }
+  // branch-free query loads (heads past G read head G-1 and are ignored)
+  float qf[GM][8];
 #pragma unroll
-    for (int r = 0; r < UNROLL; r++) {
-      const int c = cb + r * GROUPS;
-      if (c >= c1) break;
-      double xd[8];
+  for (int g = 0; g < GM; g++)
+    load_row8<DT>(q, (int64_t)b * Hq + (int64_t)h * G + min(g, G - 1), j, qf[g]);
 #pragma unroll
-      for (int t = 0; t < 8; t++) xd[t] = (double)x[r][t];
-      double tot = 0.0, mine = 0.0;
+  for (int r = 0; r < ROWS; r++) {
+    const int c = c0 + r * GROUPS + grp;
+    if (c >= C) break;
+    double xd[8];
+    unpack8<DT>(raw[r], xd);
+    double tot = 0.0, mine = 0.0;
 #pragma unroll
-      for (int g = 0; g < GM; g++) {
-        if (g < G) {
-          double p = 0.0;
+    for (int g = 0; g < GM; g++) {
+      if (g < G) {
+        double p = 0.0;
 #pragma unroll
-          for (int t = 0; t < 8; t++) p = __builtin_fma(qv[g][t], xd[t], p);
-          p += __shfl_xor(p, 8, 16);
-          p += __shfl_xor(p, 4, 16);
-          p += __shfl_xor(p, 2, 16);
-          p += __shfl_xor(p, 1, 16);
-          tot += p;
-          if (j == g) mine = p;
-        }
+        for (int t = 0; t < 8; t++) p = __builtin_fma((double)qf[g][t], xd[t], p);
+        p = row16_sum(p);
+        tot += p;
+        if (j == g) mine = p;
       }
-      if (j < G) S[(rowbase + c) * G + j] = (float)(mine * (double)scale);
-      if (j == 0) key[rowbase + c] = order_key((float)tot);
     }
+    if (j < G) S[(rowbase + c) * GM + j] = (float)(mine * (double)scale);
+    if (j == 0) key[rowbase + c] = order_key((float)tot);
   }
 }
 
@@ -109,17 +127,16 @@ template <int DT>
 hipError_t launch_score_dt(const DecodeArgs& a, const void* cent, const void* q,
                            const DecodeWs& ws, hipStream_t s) {
   const Geom& g = *a.g;
-  const int cpb = 256;
-  dim3 grid((g.C + cpb - 1) / cpb, g.U);
+  dim3 grid((g.C + GROUPS * ROWS - 1) / (GROUPS * ROWS), g.U);
   if (a.G <= 4)
     WI_LAUNCH(K_SCORE, (score_kernel<DT, 4>), grid, dim3(SCORE_THREADS), 0, s, cent, q,
-                       g.C, a.G, g.H, a.Hq, cpb, a.scale, ws.key, ws.S);
+              g.C, a.G, g.H, a.Hq, a.scale, ws.key, ws.S);
   else if (a.G <= 8)
     WI_LAUNCH(K_SCORE, (score_kernel<DT, 8>), grid, dim3(SCORE_THREADS), 0, s, cent, q,
-                       g.C, a.G, g.H, a.Hq, cpb, a.scale, ws.key, ws.S);
+              g.C, a.G, g.H, a.Hq, a.scale, ws.key, ws.S);
   else
     WI_LAUNCH(K_SCORE, (score_kernel<DT, 16>), grid, dim3(SCORE_THREADS), 0, s, cent, q,
-                       g.C, a.G, g.H, a.Hq, cpb, a.scale, ws.key, ws.S);
+              g.C, a.G, g.H, a.Hq, a.scale, ws.key, ws.S);
   return hipGetLastError();
 }
 

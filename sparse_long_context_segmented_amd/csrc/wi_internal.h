@@ -77,13 +77,16 @@ constexpr int KPP_SLICE = 256;  // points per k-means++ workgroup
 
 // Decode workspace.
 struct DecodeWs {
-  uint32_t* key;     // [U*C] order-preserving ranking keys
-  float* S;          // [U*C*G] scaled per-head centroid logits
-  int* R;            // [U*K_r] retrieval clusters, ascending id
-  int* E;            // [U*K_e] estimation clusters, ascending id
-  int* Rpre;         // [U*(K_r+1)] prefix sums of R cluster sizes
-  int* rank;         // [U*(K_r+K_e)] selected ids in rank order (debug path)
-  float* part;       // [U*P*G*(2+128)] chunk partials (m, l, acc)
+  uint32_t* key;       // [U*C] order-preserving ranking keys
+  float* S;            // [U*C*GS] scaled per-head centroid logits (GS = 4, 8, 16)
+  int* R;              // [U*K_r] retrieval clusters, ascending id
+  int* Rblk;           // [U*K_r] first block of each R cluster
+  int* Rpre;           // [U*(K_r+1)] prefix sums of R cluster sizes
+  int* E;              // [U*K_e] estimation clusters, ascending id
+  int* Esz;            // [U*K_e] size of each E cluster
+  int* rowtab;         // [U*n_idx] slot of each retrieved execution-buffer token
+  int* rank;           // [U*(K_r+K_e)] selected ids in rank order (debug path)
+  float* part;         // [U*P*G*(2+128)] chunk partials (m, l, acc)
 };
 
 // ---------------------------------------------------------------------------
@@ -130,6 +133,37 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Sum over each row of 16 lanes with DPP moves (no LDS round trip): xor-1
+// and xor-2 within quads, then half-row and row mirrors. Every lane of the
+// row ends with the same value (each step adds a pair in both orders, and
+// addition is commutative), so results are deterministic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(b & 0xFFFFFFFFll), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<DPP_XOR1>(v);
+  v += dpp_f32<DPP_XOR2>(v);
+  v += dpp_f32<DPP_HALF_MIRROR>(v);
+  v += dpp_f32<DPP_MIRROR>(v);
+  return v;
+}
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<DPP_XOR1>(v);
+  v += dpp_f64<DPP_XOR2>(v);
+  v += dpp_f64<DPP_HALF_MIRROR>(v);
+  v += dpp_f64<DPP_MIRROR>(v);
+  return v;
+}
 
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_sum(float v) {
@@ -188,7 +222,8 @@ struct DecodeArgs {
 };
 hipError_t launch_score(const DecodeArgs& a, const void* centroids, const void* q,
                         const DecodeWs& ws, hipStream_t s);
-hipError_t launch_select(const DecodeArgs& a, const DecodeWs& ws, hipStream_t s);
+hipError_t launch_select(const DecodeArgs& a, const wi_index_bufs& b, const DecodeWs& ws,
+                         hipStream_t s);
 hipError_t launch_attend(const DecodeArgs& a, const wi_index_bufs& b, const void* q,
                          float* out, const DecodeWs& ws, hipStream_t s);
 hipError_t launch_debug_outputs(const DecodeArgs& a, const wi_index_bufs& b,
