@@ -164,7 +164,9 @@ def main():
                 + retrieved * 128 * e * 2)
     b_out = U * G * 128 * 4
     step_bytes = b_score + b_attend + b_out
-    per_kernel = {"score": b_score, "attend": b_attend, "combine": b_out, "select": 0}
+    # score streams the centroids; select_attend gathers the retrieval zone,
+    # reads the estimation clusters' value sums and writes the output
+    per_kernel = {"score": b_score, "select_attend": b_attend + b_out}
     # the dominant kernel among those that move the method's HBM bytes
     dom = max((k for k in avg if per_kernel.get(k, 0) > 0), key=lambda k: avg[k])
     dom_bytes = per_kernel.get(dom, 0)

@@ -146,12 +146,14 @@ wi_status wi_build_index(const wi_index_desc *desc, const void *k,
 /* Decode shape. Query head j maps to KV head j / (n_q_heads / n_kv_heads). */
 typedef struct {
   int32_t n_q_heads;   /* multiple of n_kv_heads; G = Hq / Hkv <= 16      */
-  int32_t k_retrieve;  /* K_r: retrieval-zone clusters, 0 <= K_r <= C     */
+  int32_t k_retrieve;  /* K_r: retrieval-zone clusters, 0 <= K_r <= C;
+                          K_r > 4096 is WI_E_UNSUPPORTED                  */
   int32_t k_estimate;  /* K_e: estimation-zone clusters, clamped to C-K_r */
   float scale;         /* softmax scale; 0 -> 1/sqrt(head_dim)            */
 } wi_decode_desc;
 
-/* Host-only: workspace bytes for wi_decode_attention. */
+/* Host-only: workspace bytes for wi_decode_attention. Its contents on entry
+ * are ignored (the call initialises what it uses). */
 wi_status wi_decode_sizes(const wi_index_desc *desc,
                           const wi_decode_desc *ddesc, size_t *workspace_bytes);
 
@@ -174,6 +176,11 @@ wi_status wi_decode_sizes(const wi_index_desc *desc,
  *                entries past exec_cap are dropped; needs slot_token
  *   n_exec       device [U] execution-buffer length (may exceed exec_cap)
  *   bufs->assign is not read; bufs->slot_token only for exec_tokens.
+ *   Retrieved clusters are located from cluster_size alone: the index must
+ *   have block_off[c] = sum over c' < c of ceil(cluster_size[c'] / T), the
+ *   layout wi_build_index writes.
+ *   Returns WI_E_WORKSPACE if ws_bytes is below wi_decode_sizes; a unit with
+ *   no steady, retrieved or estimated token gets a zero output row.
  */
 wi_status wi_decode_attention(const wi_index_desc *desc,
                               const wi_decode_desc *ddesc,

@@ -112,7 +112,7 @@ int64_t carve_build(const wi::Geom& g, uint8_t* base, wi::BuildWs* w) {
 }
 
 struct DecodeShape {
-  int Hq, G, K_r, K_e, P;
+  int Hq, G, GS, K_r, K_e, W, PER;
   float scale;
 };
 
@@ -126,25 +126,29 @@ wi_status make_decode(const wi::Geom& g, const wi_decode_desc* dd, DecodeShape* 
   if (g.C > 65536) return fail(WI_E_UNSUPPORTED, "%d clusters per unit > 65536", g.C);
   if (dd->k_retrieve < 0 || dd->k_retrieve > g.C)
     return fail(WI_E_INVALID, "k_retrieve %d outside [0, C=%d]", dd->k_retrieve, g.C);
+  if (dd->k_retrieve > wi::RMAX)
+    return fail(WI_E_UNSUPPORTED, "k_retrieve %d > %d", dd->k_retrieve, wi::RMAX);
   if (dd->k_estimate < 0) return fail(WI_E_INVALID, "k_estimate %d < 0", dd->k_estimate);
   if (!(dd->scale >= 0.f) || !std::isfinite(dd->scale))
     return fail(WI_E_INVALID, "scale must be finite and >= 0");
   o->Hq = dd->n_q_heads;
   o->G = G;
+  o->GS = G <= 4 ? 4 : (G <= 8 ? 8 : 16);
   o->K_r = dd->k_retrieve;
   o->K_e = dd->k_estimate < g.C - dd->k_retrieve ? dd->k_estimate : g.C - dd->k_retrieve;
   o->scale = dd->scale > 0.f ? dd->scale : 1.0f / std::sqrt((float)wi::D);
-  // chunks per unit: about 64 work items (tokens or estimation clusters) each
-  const double per_cluster = (double)g.n_idx / (double)g.C;
-  const double items = g.n_st + o->K_r * per_cluster + o->K_e;
-  int P = (int)std::ceil(items / 64.0);
-  // keep the attention grid within one resident wave of workgroups when
-  // it would otherwise spill into a short second one
-  const int resident = 512;  // 2 workgroups of the attention kernel per CU
-  if ((int64_t)g.U * P > resident) P = resident / g.U;
-  if (P < 1) P = 1;
-  if (P > 1024) P = 1024;
-  o->P = P;
+  // fused kernel: about one 512-thread workgroup per CU over the whole call,
+  // at most 64 per unit, and enough that no workgroup holds more than EMAX
+  // estimation clusters
+  const int NT = wi::FUSED_THREADS;
+  const int target = 256;
+  int W = (target + g.U - 1) / g.U;
+  if (W > 64) W = 64;
+  const int wmin = (o->K_e + wi::EMAX - 1) / wi::EMAX;
+  if (W < wmin) W = wmin;
+  if (W < 1) W = 1;
+  o->W = W;
+  o->PER = g.C <= NT * 4 ? 4 : (g.C <= NT * 8 ? 8 : 16);
   return WI_OK;
 }
 
@@ -156,17 +160,14 @@ int64_t carve_decode(const wi::Geom& g, const DecodeShape& ds, uint8_t* base, wi
     return p;
   };
   wi::DecodeWs t;
-  t.key = reinterpret_cast<uint32_t*>(take((int64_t)g.U * g.C * 4));
-  const int GS = ds.G <= 4 ? 4 : (ds.G <= 8 ? 8 : 16);  // padded heads per S row
-  t.S = reinterpret_cast<float*>(take((int64_t)g.U * g.C * GS * 4 + 64));
+  const int64_t Cp = (g.C + 3) & ~3;
+  t.key = reinterpret_cast<uint32_t*>(take((int64_t)g.U * Cp * 4));
+  t.S = reinterpret_cast<float*>(take((int64_t)g.U * g.C * ds.GS * 4));
+  t.part = reinterpret_cast<float*>(take((int64_t)g.U * ds.W * ds.G * (2 + wi::D) * 4));
+  t.tix = reinterpret_cast<int*>(take((int64_t)g.U * 4));
   t.R = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_r * 4));
-  t.Rblk = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_r * 4));
-  t.Rpre = reinterpret_cast<int*>(take((int64_t)g.U * (ds.K_r + 1) * 4));
   t.E = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_e * 4));
-  t.Esz = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_e * 4));
-  t.rowtab = reinterpret_cast<int*>(take((int64_t)g.U * g.n_idx * 4));
   t.rank = reinterpret_cast<int*>(take((int64_t)g.U * (ds.K_r + ds.K_e) * 4));
-  t.part = reinterpret_cast<float*>(take((int64_t)g.U * ds.P * ds.G * (2 + wi::D) * 4));
   if (w) *w = t;
   return off;
 }
@@ -195,8 +196,7 @@ thread_local int t_cur = -1;
 
 const char* const kNames[wi::K_COUNT] = {
     "zero", "copy_init", "kpp_init", "kpp_weights", "kpp_round", "assign", "assign_fix",
-    "sort_update", "seg_scan", "layout", "score", "select", "attend", "combine", "rank",
-    "exec"};
+    "sort_update", "seg_scan", "layout", "score", "select_attend", "rank", "exec"};
 
 hipEvent_t take_event() {
   if (!t_pool.empty()) {
@@ -382,12 +382,12 @@ wi_status wi_decode_attention(const wi_index_desc* desc, const wi_decode_desc* d
   if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
   wi::DecodeWs w;
   carve_decode(g, ds, reinterpret_cast<uint8_t*>(ws), &w);
-  wi::DecodeArgs a{&g, ds.Hq, ds.G, ds.K_r, ds.K_e, ds.P, ds.scale, bufs->cluster_size};
+  wi::DecodeArgs a{&g, ds.Hq, ds.G, ds.GS, ds.K_r, ds.K_e, ds.W, ds.PER, ds.scale};
+  const bool want_lists = sel_ids || exec_tokens || n_exec;
 
   CHECK_HIP(wi::launch_score(a, bufs->centroids, q, w, stream), "score");
-  CHECK_HIP(wi::launch_select(a, *bufs, w, stream), "select");
-  CHECK_HIP(wi::launch_attend(a, *bufs, q, out, w, stream), "attend");
-  if (sel_ids || exec_tokens || n_exec)
+  CHECK_HIP(wi::launch_fused(a, *bufs, q, out, w, want_lists, stream), "select/attend");
+  if (want_lists)
     CHECK_HIP(wi::launch_debug_outputs(a, *bufs, w, sel_ids, exec_tokens, n_exec, exec_cap,
                                        stream),
               "debug outputs");

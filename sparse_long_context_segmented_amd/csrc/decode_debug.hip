@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint32_t* __restrict__ 
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int* R = Rl + (int64_t)u * K_r;
   const int* E = El + (int64_t)u * K_e;
-  const uint32_t* key = keys + (int64_t)u * C;
+  const uint32_t* key = keys + (int64_t)u * ((C + 3) & ~3);
   if (i >= M) return;
   const int c = i < K_r ? R[i] : E[i - K_r];
   const uint32_t k = key[c];

@@ -3,84 +3,139 @@
 // query the wave index for the key cluster ids; section 3.3: estimation from
 // centroid vectors).
 //
-// Memory-bound: each centroid row (128 x dtype) is read once from HBM. A
-// group of 16 lanes owns one row, each lane 8 consecutive dims loaded with a
-// single 128-bit (bf16) or 2x128-bit (fp32) load, so a wave64 streams four
-// 256-byte rows per load instruction. The per-head dot products are reduced
-// across the 16 lanes with a fixed butterfly, so results are deterministic.
+// Outputs per cluster c of unit u:
+//   key[u][c]   order-preserving bits of g_c = sum_h <q_h, mu_c> rounded to
+//               float32 once (the ranking key);
+//   S[u][c][h]  scale * <q_h, mu_c> per query head h of the group (float32,
+//               rows padded to GS = 4, 8 or 16 heads) -- the estimation-zone
+//               logits.
+// Both are read back by the fused select/attend kernel. The launch also
+// clears the per-unit arrival counters that kernel uses.
 //
-// Outputs per cluster c:  S[c][h] = scale * <q_h, mu_c>  (fp32, per head; rows
-//                                    padded to GM = 4, 8 or 16 heads)
-//                         key[c]  = order-preserving bits of sum_h <q_h, mu_c>
+// bf16 (the hot path): HBM-bound streaming of C x 256-byte rows. A wave owns
+// tiles of 16 centroid rows; lane i loads row (i % 16), 16-byte pieces at
+// dims 32 s + 8 (i / 16) for s = 0..3, so each load instruction reads 64
+// contiguous bytes of 16 rows. The same registers feed
+//   - the per-head logits: four v_mfma_f32_16x16x32_bf16 per tile with the
+//     query heads as the 16 columns of the B operand (fp32 accumulation of
+//     exact bf16 products);
+//   - the ranking key: sum_t Q_t mu_t in float64 with Q = sum_h q_h formed
+//     once in float64 (sums and products of bf16 values are exact there, so
+//     the key is the exactly rounded group score), one FMA per element in
+//     a fixed order, then a fixed two-step exchange across the four lanes
+//     that share a row.
+// fp32 (parity-size workloads only): 16 lanes per row, per-head float64 dot
+// products reduced across the row with a fixed butterfly.
 #include "wi_internal.h"
 
 namespace wi {
 namespace {
 
-constexpr int SCORE_THREADS = 256;
-constexpr int GROUPS = SCORE_THREADS / 16;  // rows in flight per step
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int DT>
-__device__ __forceinline__ void load_row8(const void* base, int64_t row, int j, float x[8]) {
-  if constexpr (DT == WI_BF16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(base) + row * D + 8 * j);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+constexpr int SCORE_THREADS = 256;
+constexpr int TPW = 2;  // 16-row tiles per wave (bf16 kernel)
+
+__device__ __forceinline__ void clear_counters(int* p, int n) {
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+template <int GS>
+__global__ __launch_bounds__(SCORE_THREADS) void score_bf16_kernel(
+    const uint16_t* __restrict__ cent, const uint16_t* __restrict__ q, int C, int Cp, int G,
+    int H, int Hq, float scale, uint32_t* __restrict__ key, float* __restrict__ S,
+    int* __restrict__ counters, int n_counters) {
+  clear_counters(counters, n_counters);
+  const int u = blockIdx.y;
+  const int b = u / H, h = u % H;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int tile0 = (blockIdx.x * (SCORE_THREADS / 64) + wv) * TPW;
+  const int64_t ubase = (int64_t)u * C;
+
+  // centroid rows first (row index clamped into the unit; rows past C are
+  // read again and never written)
+  uint4 a[TPW][4];
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-      x[2 * t] = __uint_as_float(w[t] << 16);
-      x[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+  for (int t = 0; t < TPW; t++) {
+    const int row = min((tile0 + t) * 16 + r16, C - 1);
+    const uint16_t* rp = cent + (ubase + row) * D + 8 * kg;
+#pragma unroll
+    for (int s = 0; s < 4; s++) a[t][s] = *reinterpret_cast<const uint4*>(rp + 32 * s);
+  }
+  // query heads of the group: B operand (column r16 = head r16) and Q
+  const uint16_t* qb = q + ((int64_t)b * Hq + (int64_t)h * G) * D + 8 * kg;
+  uint4 bq[4];
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const uint4 v = *reinterpret_cast<const uint4*>(qb + (int64_t)min(r16, G - 1) * D + 32 * s);
+    bq[s] = r16 < G ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
+  double Q[4][8];
+#pragma unroll
+  for (int s = 0; s < 4; s++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) Q[s][e] = 0.0;
+  // all G head loads are issued together (compile-time trip count)
+#pragma unroll
+  for (int g = 0; g < GS; g++) {
+    if (g >= G) break;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qb + (int64_t)g * D + 32 * s);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        Q[s][2 * e] += (double)__uint_as_float(w[e] << 16);
+        Q[s][2 * e + 1] += (double)__uint_as_float(w[e] & 0xFFFF0000u);
+      }
     }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(
-        reinterpret_cast<const float*>(base) + row * D + 8 * j);
-    const float4 a = p[0], b = p[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+
+#pragma unroll
+  for (int t = 0; t < TPW; t++) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    double p = 0.0;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[t][s]),
+                                                    __builtin_bit_cast(bf16x8_t, bq[s]), acc,
+                                                    0, 0, 0);
+      const uint32_t w[4] = {a[t][s].x, a[t][s].y, a[t][s].z, a[t][s].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        p = __builtin_fma(Q[s][2 * e], (double)__uint_as_float(w[e] << 16), p);
+        p = __builtin_fma(Q[s][2 * e + 1], (double)__uint_as_float(w[e] & 0xFFFF0000u), p);
+      }
+    }
+    // lanes r16, r16+16, r16+32, r16+48 hold the four 32-dim pieces of row r16
+    p += __shfl_xor(p, 16, 64);
+    p += __shfl_xor(p, 32, 64);
+    const int row = (tile0 + t) * 16 + r16;
+    if (kg == 0 && row < C) key[(int64_t)u * Cp + row] = order_key((float)p);
+    // D layout: lane holds rows 4 kg + j (j = 0..3) of the tile, column r16
+    if (r16 < G) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int rj = (tile0 + t) * 16 + 4 * kg + j;
+        if (rj < C) S[(ubase + rj) * GS + r16] = acc[j] * scale;
+      }
+    }
   }
 }
 
-// Per-head dot products are accumulated in float64: bf16 x bf16 (and fp32 x
-// fp32) products are exact in float64 and on gfx950 a float64 FMA issues at
-// the float32 rate, so the group score is exact up to the final rounding to
-// float32 that the ranking is taken in.
-//
-// Latency: the whole score pass moves a few tens of MB, so every lane issues
-// all of its row loads (ROWS per 16-lane group, one 16-byte load each) before
-// any arithmetic; a workgroup covers GROUPS * ROWS rows.
+// fp32 centroids: 16 lanes per row, per-head float64 dots.
+constexpr int GROUPS = SCORE_THREADS / 16;
 constexpr int ROWS = 4;
 
-template <int DT>
-__device__ __forceinline__ void raw_row(const void* base, int64_t row, int j, uint4 r[2]) {
-  if constexpr (DT == WI_BF16) {
-    r[0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + row * D + 8 * j);
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + row * D + 8 * j);
-    r[0] = p[0];
-    r[1] = p[1];
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ void unpack8(const uint4 r[2], double xd[8]) {
-  if constexpr (DT == WI_BF16) {
-    const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-      xd[2 * t] = (double)__uint_as_float(w[t] << 16);
-      xd[2 * t + 1] = (double)__uint_as_float(w[t] & 0xFFFF0000u);
-    }
-  } else {
-    const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
-#pragma unroll
-    for (int t = 0; t < 8; t++) xd[t] = (double)__uint_as_float(w[t]);
-  }
-}
-
-template <int DT, int GM>
-__global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
-    const void* __restrict__ cent, const void* __restrict__ q, int C, int G, int H,
-    int Hq, float scale, uint32_t* __restrict__ key, float* __restrict__ S) {
+template <int GM>
+__global__ __launch_bounds__(SCORE_THREADS) void score_f32_kernel(
+    const float* __restrict__ cent, const float* __restrict__ q, int C, int Cp, int G, int H,
+    int Hq, float scale, uint32_t* __restrict__ key, float* __restrict__ S, int* __restrict__ counters,
+    int n_counters) {
+  clear_counters(counters, n_counters);
   const int u = blockIdx.y;
   const int b = u / H, h = u % H;
   const int tid = threadIdx.x;
@@ -88,24 +143,28 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
   const int c0 = blockIdx.x * (GROUPS * ROWS);
   const int64_t rowbase = (int64_t)u * C;
 
-  // issue the row loads first
-  uint4 raw[ROWS][2];
+  float4 raw[ROWS][2];
 #pragma unroll
   for (int r = 0; r < ROWS; r++) {
-    const int c = c0 + r * GROUPS + grp;
-    if (c < C) raw_row<DT>(cent, rowbase + c, j, raw[r]);
+    const int c = min(c0 + r * GROUPS + grp, C - 1);
+    const float4* p = reinterpret_cast<const float4*>(cent + (rowbase + c) * D + 8 * j);
+    raw[r][0] = p[0];
+    raw[r][1] = p[1];
   }
-  // branch-free query loads (heads past G read head G-1 and are ignored)
   float qf[GM][8];
 #pragma unroll
-  for (int g = 0; g < GM; g++)
-    load_row8<DT>(q, (int64_t)b * Hq + (int64_t)h * G + min(g, G - 1), j, qf[g]);
+  for (int g = 0; g < GM; g++) {
+    const float4* p = reinterpret_cast<const float4*>(
+        q + ((int64_t)b * Hq + (int64_t)h * G + min(g, G - 1)) * D + 8 * j);
+    const float4 x = p[0], y = p[1];
+    qf[g][0] = x.x; qf[g][1] = x.y; qf[g][2] = x.z; qf[g][3] = x.w;
+    qf[g][4] = y.x; qf[g][5] = y.y; qf[g][6] = y.z; qf[g][7] = y.w;
+  }
 #pragma unroll
   for (int r = 0; r < ROWS; r++) {
     const int c = c0 + r * GROUPS + grp;
-    if (c >= C) break;
-    double xd[8];
-    unpack8<DT>(raw[r], xd);
+    const double xd[8] = {raw[r][0].x, raw[r][0].y, raw[r][0].z, raw[r][0].w,
+                          raw[r][1].x, raw[r][1].y, raw[r][1].z, raw[r][1].w};
     double tot = 0.0, mine = 0.0;
 #pragma unroll
     for (int g = 0; g < GM; g++) {
@@ -118,34 +177,44 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
         if (j == g) mine = p;
       }
     }
-    if (j < G) S[(rowbase + c) * GM + j] = (float)(mine * (double)scale);
-    if (j == 0) key[rowbase + c] = order_key((float)tot);
+    if (c < C) {
+      if (j < G) S[(rowbase + c) * GM + j] = (float)(mine * (double)scale);
+      if (j == 0) key[(int64_t)u * Cp + c] = order_key((float)tot);
+    }
   }
-}
-
-template <int DT>
-hipError_t launch_score_dt(const DecodeArgs& a, const void* cent, const void* q,
-                           const DecodeWs& ws, hipStream_t s) {
-  const Geom& g = *a.g;
-  dim3 grid((g.C + GROUPS * ROWS - 1) / (GROUPS * ROWS), g.U);
-  if (a.G <= 4)
-    WI_LAUNCH(K_SCORE, (score_kernel<DT, 4>), grid, dim3(SCORE_THREADS), 0, s, cent, q,
-              g.C, a.G, g.H, a.Hq, a.scale, ws.key, ws.S);
-  else if (a.G <= 8)
-    WI_LAUNCH(K_SCORE, (score_kernel<DT, 8>), grid, dim3(SCORE_THREADS), 0, s, cent, q,
-              g.C, a.G, g.H, a.Hq, a.scale, ws.key, ws.S);
-  else
-    WI_LAUNCH(K_SCORE, (score_kernel<DT, 16>), grid, dim3(SCORE_THREADS), 0, s, cent, q,
-              g.C, a.G, g.H, a.Hq, a.scale, ws.key, ws.S);
-  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_score(const DecodeArgs& a, const void* cent, const void* q,
                         const DecodeWs& ws, hipStream_t s) {
-  return a.g->dtype == WI_BF16 ? launch_score_dt<WI_BF16>(a, cent, q, ws, s)
-                               : launch_score_dt<WI_F32>(a, cent, q, ws, s);
+  const Geom& g = *a.g;
+  if (g.dtype == WI_BF16) {
+    const int tiles = (g.C + 15) / 16;
+    const int per_wg = (SCORE_THREADS / 64) * TPW;
+    dim3 grid((tiles + per_wg - 1) / per_wg, g.U);
+    const uint16_t* c16 = reinterpret_cast<const uint16_t*>(cent);
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
+#define WI_SC(GSV)                                                                          \
+  WI_LAUNCH(K_SCORE, (score_bf16_kernel<GSV>), grid, dim3(SCORE_THREADS), 0, s, c16, q16,   \
+            g.C, (g.C + 3) & ~3, a.G, g.H, a.Hq, a.scale, ws.key, ws.S, ws.tix, g.U)
+    if (a.GS == 4) WI_SC(4);
+    else if (a.GS == 8) WI_SC(8);
+    else WI_SC(16);
+#undef WI_SC
+  } else {
+    dim3 grid((g.C + GROUPS * ROWS - 1) / (GROUPS * ROWS), g.U);
+    const float* c32 = reinterpret_cast<const float*>(cent);
+    const float* q32 = reinterpret_cast<const float*>(q);
+#define WI_SC(GSV)                                                                          \
+  WI_LAUNCH(K_SCORE, (score_f32_kernel<GSV>), grid, dim3(SCORE_THREADS), 0, s, c32, q32,    \
+            g.C, (g.C + 3) & ~3, a.G, g.H, a.Hq, a.scale, ws.key, ws.S, ws.tix, g.U)
+    if (a.GS == 4) WI_SC(4);
+    else if (a.GS == 8) WI_SC(8);
+    else WI_SC(16);
+#undef WI_SC
+  }
+  return hipGetLastError();
 }
 
 }  // namespace wi

@@ -77,17 +77,22 @@ constexpr int KPP_SLICE = 256;  // points per k-means++ workgroup
 
 // Decode workspace.
 struct DecodeWs {
-  uint32_t* key;       // [U*C] order-preserving ranking keys
+  uint32_t* key;       // [U][Cp] order-preserving ranking keys (Cp = C rounded up to 4)
   float* S;            // [U*C*GS] scaled per-head centroid logits (GS = 4, 8, 16)
-  int* R;              // [U*K_r] retrieval clusters, ascending id
-  int* Rblk;           // [U*K_r] first block of each R cluster
-  int* Rpre;           // [U*(K_r+1)] prefix sums of R cluster sizes
-  int* E;              // [U*K_e] estimation clusters, ascending id
-  int* Esz;            // [U*K_e] size of each E cluster
-  int* rowtab;         // [U*n_idx] slot of each retrieved execution-buffer token
-  int* rank;           // [U*(K_r+K_e)] selected ids in rank order (debug path)
-  float* part;         // [U*P*G*(2+128)] chunk partials (m, l, acc)
+  float* part;         // [U*W*G*(2+128)] per-workgroup partials (m, l, acc)
+  int* tix;            // [U] arrival counters of the fused kernel
+  int* R;              // [U*K_r] retrieval clusters, ascending id (debug outputs only)
+  int* E;              // [U*K_e] estimation clusters, ascending id (debug outputs only)
+  int* rank;           // [U*(K_r+K_e)] selected ids in rank order (debug outputs only)
 };
+
+// Fused decode kernel limits: retrieval clusters held in LDS (k_retrieve <=
+// RMAX), and estimation clusters per workgroup (the host picks W so that
+// ceil(K_e / W) <= EMAX).
+constexpr int RMAX = 4096;
+constexpr int EMAX = 2048;
+// Threads per workgroup of the fused decode kernel.
+constexpr int FUSED_THREADS = 512;
 
 // ---------------------------------------------------------------------------
 // Device helpers.
@@ -182,7 +187,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // thread. Kernel name ids index a fixed table.
 enum KernelId {
   K_ZERO, K_COPY, K_KPP_INIT, K_KPP_WEIGHTS, K_KPP_ROUND, K_ASSIGN, K_ASSIGN_FIX,
-  K_SORT_UPDATE, K_SEG_SCAN, K_LAYOUT, K_SCORE, K_SELECT, K_ATTEND, K_COMBINE, K_RANK,
+  K_SORT_UPDATE, K_SEG_SCAN, K_LAYOUT, K_SCORE, K_FUSED, K_RANK,
   K_EXEC, K_COUNT
 };
 void tmark_begin(KernelId id, hipStream_t s);
@@ -216,16 +221,15 @@ hipError_t launch_layout(const Geom& g, const void* K, const void* V,
 
 struct DecodeArgs {
   const Geom* g;
-  int Hq, G, K_r, K_e, P;
+  int Hq, G, GS, K_r, K_e;  // K_e already clamped to C - K_r
+  int W;                    // fused-kernel workgroups per unit
+  int PER;                  // keys per thread and pass in the fused kernel (4, 8, 16)
   float scale;
-  const int32_t* sizes;  // cluster sizes [U][C]
 };
 hipError_t launch_score(const DecodeArgs& a, const void* centroids, const void* q,
                         const DecodeWs& ws, hipStream_t s);
-hipError_t launch_select(const DecodeArgs& a, const wi_index_bufs& b, const DecodeWs& ws,
-                         hipStream_t s);
-hipError_t launch_attend(const DecodeArgs& a, const wi_index_bufs& b, const void* q,
-                         float* out, const DecodeWs& ws, hipStream_t s);
+hipError_t launch_fused(const DecodeArgs& a, const wi_index_bufs& b, const void* q,
+                        float* out, const DecodeWs& ws, bool want_lists, hipStream_t s);
 hipError_t launch_debug_outputs(const DecodeArgs& a, const wi_index_bufs& b,
                                 const DecodeWs& ws, int32_t* sel_ids,
                                 int32_t* exec_tokens, int32_t* n_exec,

@@ -164,4 +164,9 @@ def test_decode_sizes_grow_with_budget(L):
     b = wi.decode_sizes(d, wi.DecodeDesc(32, 1000, 4000, 0.0))
     assert b > a > 8 * 8192 * 4
     # K_e is clamped to C - K_r
-    assert wi.decode_sizes(d, wi.DecodeDesc(32, 8192, 5000, 0.0)) > 0
+    assert wi.decode_sizes(d, wi.DecodeDesc(32, 4096, 5000, 0.0)) == \
+        wi.decode_sizes(d, wi.DecodeDesc(32, 4096, 4096, 0.0))
+    # the retrieval zone is held on chip: more than 4096 clusters is unsupported
+    with pytest.raises(wi.WIError) as ei:
+        wi.decode_sizes(d, wi.DecodeDesc(32, 4097, 10, 0.0))
+    assert ei.value.status == 2
