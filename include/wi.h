@@ -146,10 +146,15 @@ wi_status wi_build_index(const wi_index_desc *desc, const void *k,
 /* Decode shape. Query head j maps to KV head j / (n_q_heads / n_kv_heads). */
 typedef struct {
   int32_t n_q_heads;   /* multiple of n_kv_heads; G = Hq / Hkv <= 16      */
-  int32_t k_retrieve;  /* K_r: retrieval-zone clusters, 0 <= K_r <= C;
-                          K_r > 4096 is WI_E_UNSUPPORTED                  */
+  int32_t k_retrieve;  /* K_r: retrieval-zone clusters, 0 <= K_r <= C      */
   int32_t k_estimate;  /* K_e: estimation-zone clusters, clamped to C-K_r */
   float scale;         /* softmax scale; 0 -> 1/sqrt(head_dim)            */
+  int32_t wg_per_unit; /* workgroups per (sequence, KV head) of the fused
+                          kernel: 0 = automatic (about one per compute
+                          unit over the call); 1..64 = that many, at most
+                          one per 16 clusters. Results agree to rounding
+                          order across choices; each choice is itself
+                          deterministic                                    */
 } wi_decode_desc;
 
 /* Host-only: workspace bytes for wi_decode_attention. Its contents on entry
@@ -175,10 +180,10 @@ wi_status wi_decode_sizes(const wi_index_desc *desc,
  *                cluster's members (rank order, ascending position);
  *                entries past exec_cap are dropped; needs slot_token
  *   n_exec       device [U] execution-buffer length (may exceed exec_cap)
- *   bufs->assign is not read; bufs->slot_token only for exec_tokens.
- *   Retrieved clusters are located from cluster_size alone: the index must
- *   have block_off[c] = sum over c' < c of ceil(cluster_size[c'] / T), the
- *   layout wi_build_index writes.
+ *   bufs->assign is not read; bufs->slot_token only for exec_tokens. The
+ *   index must be one wi_build_index wrote (cluster c's members in the
+ *   first cluster_size[c] slots from block block_off[c], within block_cap).
+ *   NaN in q or the centroids leaves the selection unspecified (no fault).
  *   Returns WI_E_WORKSPACE if ws_bytes is below wi_decode_sizes; a unit with
  *   no steady, retrieved or estimated token gets a zero output row.
  */

@@ -112,7 +112,7 @@ int64_t carve_build(const wi::Geom& g, uint8_t* base, wi::BuildWs* w) {
 }
 
 struct DecodeShape {
-  int Hq, G, GS, K_r, K_e, W, PER;
+  int Hq, G, GS, K_r, K_e, W;
   float scale;
 };
 
@@ -126,29 +126,26 @@ wi_status make_decode(const wi::Geom& g, const wi_decode_desc* dd, DecodeShape* 
   if (g.C > 65536) return fail(WI_E_UNSUPPORTED, "%d clusters per unit > 65536", g.C);
   if (dd->k_retrieve < 0 || dd->k_retrieve > g.C)
     return fail(WI_E_INVALID, "k_retrieve %d outside [0, C=%d]", dd->k_retrieve, g.C);
-  if (dd->k_retrieve > wi::RMAX)
-    return fail(WI_E_UNSUPPORTED, "k_retrieve %d > %d", dd->k_retrieve, wi::RMAX);
   if (dd->k_estimate < 0) return fail(WI_E_INVALID, "k_estimate %d < 0", dd->k_estimate);
   if (!(dd->scale >= 0.f) || !std::isfinite(dd->scale))
     return fail(WI_E_INVALID, "scale must be finite and >= 0");
+  if (dd->wg_per_unit < 0 || dd->wg_per_unit > wi::MAX_WG)
+    return fail(WI_E_INVALID, "wg_per_unit %d outside [0, %d]", dd->wg_per_unit, wi::MAX_WG);
   o->Hq = dd->n_q_heads;
   o->G = G;
   o->GS = G <= 4 ? 4 : (G <= 8 ? 8 : 16);
   o->K_r = dd->k_retrieve;
   o->K_e = dd->k_estimate < g.C - dd->k_retrieve ? dd->k_estimate : g.C - dd->k_retrieve;
   o->scale = dd->scale > 0.f ? dd->scale : 1.0f / std::sqrt((float)wi::D);
-  // fused kernel: about one 512-thread workgroup per CU over the whole call,
-  // at most 64 per unit, and enough that no workgroup holds more than EMAX
-  // estimation clusters
-  const int NT = wi::FUSED_THREADS;
-  const int target = 256;
-  int W = (target + g.U - 1) / g.U;
-  if (W > 64) W = 64;
-  const int wmin = (o->K_e + wi::EMAX - 1) / wi::EMAX;
-  if (W < wmin) W = wmin;
+  // fused kernel: the caller's count, or about one workgroup per CU over the
+  // whole call; at most MAX_WG per unit and no more than the unit's
+  // 16-cluster ownership groups
+  int W = dd->wg_per_unit > 0 ? dd->wg_per_unit : (256 + g.U - 1) / g.U;
+  const int groups = (g.C + 15) / 16;
+  if (W > groups) W = groups;
+  if (W > wi::MAX_WG) W = wi::MAX_WG;
   if (W < 1) W = 1;
   o->W = W;
-  o->PER = g.C <= NT * 4 ? 4 : (g.C <= NT * 8 ? 8 : 16);
   return WI_OK;
 }
 
@@ -165,8 +162,7 @@ int64_t carve_decode(const wi::Geom& g, const DecodeShape& ds, uint8_t* base, wi
   t.S = reinterpret_cast<float*>(take((int64_t)g.U * g.C * ds.GS * 4));
   t.part = reinterpret_cast<float*>(take((int64_t)g.U * ds.W * ds.G * (2 + wi::D) * 4));
   t.tix = reinterpret_cast<int*>(take((int64_t)g.U * 4));
-  t.R = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_r * 4));
-  t.E = reinterpret_cast<int*>(take((int64_t)g.U * ds.K_e * 4));
+  t.zone = take((int64_t)g.U * g.C);
   t.rank = reinterpret_cast<int*>(take((int64_t)g.U * (ds.K_r + ds.K_e) * 4));
   if (w) *w = t;
   return off;
@@ -382,7 +378,7 @@ wi_status wi_decode_attention(const wi_index_desc* desc, const wi_decode_desc* d
   if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
   wi::DecodeWs w;
   carve_decode(g, ds, reinterpret_cast<uint8_t*>(ws), &w);
-  wi::DecodeArgs a{&g, ds.Hq, ds.G, ds.GS, ds.K_r, ds.K_e, ds.W, ds.PER, ds.scale};
+  wi::DecodeArgs a{&g, ds.Hq, ds.G, ds.GS, ds.K_r, ds.K_e, ds.W, ds.scale};
   const bool want_lists = sel_ids || exec_tokens || n_exec;
 
   CHECK_HIP(wi::launch_score(a, bufs->centroids, q, w, stream), "score");

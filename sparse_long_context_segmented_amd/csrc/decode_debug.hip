@@ -8,28 +8,23 @@
 namespace wi {
 namespace {
 
-// rank(c) = #{selected c' : key(c') > key(c), or equal keys and c' < c}
+// For every selected cluster c (zone != 0):
+// rank(c) = #{selected c' : key(c') > key(c), or equal keys and c' < c}.
 __global__ __launch_bounds__(256) void rank_kernel(const uint32_t* __restrict__ keys,
-                                                   const int* __restrict__ Rl,
-                                                   const int* __restrict__ El, int C,
-                                                   int K_r, int K_e,
-                                                   int32_t* __restrict__ ranked) {
+                                                   const uint8_t* __restrict__ zones, int C,
+                                                   int M, int32_t* __restrict__ ranked) {
   const int u = blockIdx.y;
-  const int M = K_r + K_e;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int* R = Rl + (int64_t)u * K_r;
-  const int* E = El + (int64_t)u * K_e;
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
   const uint32_t* key = keys + (int64_t)u * ((C + 3) & ~3);
-  if (i >= M) return;
-  const int c = i < K_r ? R[i] : E[i - K_r];
+  const uint8_t* zone = zones + (int64_t)u * C;
+  if (c >= C || zone[c] == 0) return;
   const uint32_t k = key[c];
   int rank = 0;
-  for (int jj = 0; jj < M; jj++) {
-    const int c2 = jj < K_r ? R[jj] : E[jj - K_r];
+  for (int c2 = 0; c2 < C; c2++) {
     const uint32_t k2 = key[c2];
-    rank += (k2 > k) || (k2 == k && c2 < c);
+    rank += zone[c2] != 0 && ((k2 > k) || (k2 == k && c2 < c));
   }
-  ranked[(int64_t)u * M + rank] = c;
+  if (rank < M) ranked[(int64_t)u * M + rank] = c;
 }
 
 __global__ __launch_bounds__(256) void exec_kernel(
@@ -54,7 +49,8 @@ __global__ __launch_bounds__(256) void exec_kernel(
   __syncthreads();
   for (int base = 0; base < K_r; base += 256) {
     const int r = base + tid;
-    const int c = r < K_r ? rk[r] : -1;
+    const int c0 = r < K_r ? rk[r] : -1;
+    const int c = c0 >= 0 && c0 < C ? c0 : -1;
     const int n = c >= 0 ? sz[c] : 0;
     // block exclusive scan of n
     int x = n;
@@ -90,9 +86,8 @@ hipError_t launch_debug_outputs(const DecodeArgs& a, const wi_index_bufs& b,
   const int M = a.K_r + a.K_e;
   int32_t* ranked = sel_ids ? sel_ids : ws.rank;
   if (M > 0) {
-    dim3 grid((M + 255) / 256, g.U);
-    WI_LAUNCH(K_RANK, rank_kernel, grid, dim3(256), 0, s, ws.key, ws.R, ws.E, g.C, a.K_r,
-                       a.K_e, ranked);
+    dim3 grid((g.C + 255) / 256, g.U);
+    WI_LAUNCH(K_RANK, rank_kernel, grid, dim3(256), 0, s, ws.key, ws.zone, g.C, M, ranked);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

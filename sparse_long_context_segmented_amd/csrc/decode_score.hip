@@ -44,9 +44,9 @@ __device__ __forceinline__ void clear_counters(int* p, int n) {
 
 template <int GS>
 __global__ __launch_bounds__(SCORE_THREADS) void score_bf16_kernel(
-    const uint16_t* __restrict__ cent, const uint16_t* __restrict__ q, int C, int Cp, int G,
-    int H, int Hq, float scale, uint32_t* __restrict__ key, float* __restrict__ S,
-    int* __restrict__ counters, int n_counters) {
+    const uint16_t* __restrict__ cent, const uint16_t* __restrict__ q,
+    int C, int Cp, int G, int H, int Hq, float scale, uint32_t* __restrict__ key,
+    float* __restrict__ S, int* __restrict__ counters, int n_counters) {
   clear_counters(counters, n_counters);
   const int u = blockIdx.y;
   const int b = u / H, h = u % H;
@@ -132,9 +132,9 @@ constexpr int ROWS = 4;
 
 template <int GM>
 __global__ __launch_bounds__(SCORE_THREADS) void score_f32_kernel(
-    const float* __restrict__ cent, const float* __restrict__ q, int C, int Cp, int G, int H,
-    int Hq, float scale, uint32_t* __restrict__ key, float* __restrict__ S, int* __restrict__ counters,
-    int n_counters) {
+    const float* __restrict__ cent, const float* __restrict__ q,
+    int C, int Cp, int G, int H, int Hq, float scale, uint32_t* __restrict__ key,
+    float* __restrict__ S, int* __restrict__ counters, int n_counters) {
   clear_counters(counters, n_counters);
   const int u = blockIdx.y;
   const int b = u / H, h = u % H;

@@ -81,18 +81,14 @@ struct DecodeWs {
   float* S;            // [U*C*GS] scaled per-head centroid logits (GS = 4, 8, 16)
   float* part;         // [U*W*G*(2+128)] per-workgroup partials (m, l, acc)
   int* tix;            // [U] arrival counters of the fused kernel
-  int* R;              // [U*K_r] retrieval clusters, ascending id (debug outputs only)
-  int* E;              // [U*K_e] estimation clusters, ascending id (debug outputs only)
+  uint8_t* zone;       // [U*C] 1 retrieval, 2 estimation, 0 neither (debug outputs only)
   int* rank;           // [U*(K_r+K_e)] selected ids in rank order (debug outputs only)
 };
 
-// Fused decode kernel limits: retrieval clusters held in LDS (k_retrieve <=
-// RMAX), and estimation clusters per workgroup (the host picks W so that
-// ceil(K_e / W) <= EMAX).
-constexpr int RMAX = 4096;
-constexpr int EMAX = 2048;
-// Threads per workgroup of the fused decode kernel.
+// Threads per workgroup of the fused decode kernel; partials merged per unit
+// by its last workgroup (at most MAX_WG workgroups per unit).
 constexpr int FUSED_THREADS = 512;
+constexpr int MAX_WG = 64;
 
 // ---------------------------------------------------------------------------
 // Device helpers.
@@ -222,8 +218,7 @@ hipError_t launch_layout(const Geom& g, const void* K, const void* V,
 struct DecodeArgs {
   const Geom* g;
   int Hq, G, GS, K_r, K_e;  // K_e already clamped to C - K_r
-  int W;                    // fused-kernel workgroups per unit
-  int PER;                  // keys per thread and pass in the fused kernel (4, 8, 16)
+  int W;                    // fused-kernel workgroups per unit (<= MAX_WG)
   float scale;
 };
 hipError_t launch_score(const DecodeArgs& a, const void* centroids, const void* q,

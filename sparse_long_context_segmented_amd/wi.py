@@ -49,7 +49,8 @@ class IndexBufs(ctypes.Structure):
 
 class DecodeDesc(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("k_retrieve", ctypes.c_int32),
-                ("k_estimate", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("k_estimate", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("wg_per_unit", ctypes.c_int32)]
 
 
 _lib = None

@@ -17,10 +17,10 @@ pytestmark = pytest.mark.gpu
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 
 
-def _run(w, k_r, k_e, n_iters=2, batch=None, want_debug=True, scale=0.0):
+def _run(w, k_r, k_e, n_iters=2, batch=None, want_debug=True, scale=0.0, wg=0):
     print(f"[decode parity] {w.name} dtype={w.dtype} B={w.batch} H={w.n_kv_heads} "
           f"G={w.group} N={w.n_ctx} seg={w.seg_len} k={w.clusters_per_seg} "
-          f"K_r={k_r} K_e={k_e}", flush=True)
+          f"K_r={k_r} K_e={k_e} wg={wg}", flush=True)
     K, V, q = synth.gen_batch(w)
     od = oracle.make_desc(w.dtype, w.batch, w.n_kv_heads, w.n_ctx, seg_len=w.seg_len,
                           clusters_per_seg=w.clusters_per_seg, n_iters=n_iters)
@@ -33,7 +33,7 @@ def _run(w, k_r, k_e, n_iters=2, batch=None, want_debug=True, scale=0.0):
     U = w.batch * w.n_kv_heads
     k_e_eff = min(k_e, C - k_r)
     M = k_r + k_e_eff
-    dd = wi.DecodeDesc(w.n_q_heads, k_r, k_e, scale)
+    dd = wi.DecodeDesc(w.n_q_heads, k_r, k_e, scale, wg)
     sel = exe = nexe = None
     exec_cap = 68 + int(np.sort(idx["sizes"], axis=1)[:, ::-1][:, :k_r].sum(axis=1).max(initial=0))
     if want_debug:
@@ -130,3 +130,25 @@ def test_decode_deterministic():
         outs.append(o.cpu().numpy())
     assert np.array_equal(outs[0].view(np.uint32), r["out"].view(np.uint32))
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+# 562 clusters per unit (four segments of 128 and a short one of 50): with one
+# workgroup per unit its own clusters come in two chunks of 512, and K_r = 400
+# gives it thousands of retrieved tokens (many rounds); three workgroups give
+# each an interleaved share with a partial last group of 16 ids.
+MULTI = synth.custom(220, "bf16", 1, 8, 2, 68 + 4 * 1024 + 50, 1024, 128, n_needles=4)
+
+
+@pytest.mark.parametrize("wg", [1, 3, 64])
+def test_decode_multichunk_and_workgroup_counts(wg):
+    r = _run(MULTI, 400, 150, wg=wg)
+    assert r["C"] == 562
+    assert r["mism"] == 0
+    assert r["err"] <= TOL["bf16"]
+
+
+def test_decode_multichunk_fp32():
+    w = synth.custom(221, "f32", 1, 4, 1, 68 + 4 * 1024 + 50, 1024, 128, n_needles=4)
+    r = _run(w, 37, 300, wg=1)
+    assert r["mism"] == 0
+    assert r["err"] <= TOL["f32"]
