@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's timed CPU work")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--wg", type=int, default=0,
+                    help="fused-kernel workgroups per (sequence, KV head); 0 = automatic")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3 (no CPU leg, few steps)")
     return ap.parse_args()
@@ -118,7 +120,7 @@ def main():
 
     # ---- decode: R index copies at distinct addresses ----
     k_r, k_e = w.budgets()
-    dd = wi.DecodeDesc(w.n_q_heads, k_r, k_e, 0.0)
+    dd = wi.DecodeDesc(w.n_q_heads, k_r, k_e, 0.0, a.wg)
     nexe = torch.empty(U, dtype=torch.int32, device=dev)
     wi.decode_attention(ix, dd, qt, n_exec=nexe)
     torch.cuda.synchronize()

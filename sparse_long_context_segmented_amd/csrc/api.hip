@@ -160,6 +160,7 @@ int64_t carve_decode(const wi::Geom& g, const DecodeShape& ds, uint8_t* base, wi
   const int64_t Cp = (g.C + 3) & ~3;
   t.key = reinterpret_cast<uint32_t*>(take((int64_t)g.U * Cp * 4));
   t.S = reinterpret_cast<float*>(take((int64_t)g.U * g.C * ds.GS * 4));
+  t.mm = reinterpret_cast<float2*>(take((int64_t)g.U * wi::score_blocks(g) * 8));
   t.part = reinterpret_cast<float*>(take((int64_t)g.U * ds.W * ds.G * (2 + wi::D) * 4));
   t.tix = reinterpret_cast<int*>(take((int64_t)g.U * 4));
   t.zone = take((int64_t)g.U * g.C);

@@ -20,9 +20,11 @@
 //     lower cluster id on equal keys. For M in {K_r, K_r + K_e'} the M-th
 //     ranked cluster -- the pivot -- is found; cluster c is among the first M
 //     iff comp(c) >= comp(pivot), comp = key << 32 | (2^32 - 1 - id). A
-//     2048-bin histogram linear in key value locates the pivot's bin; its
-//     keys (at most CAND_MAX) are ranked exactly by one wave, a fuller bin
-//     falls back to an 8-pass radix select over comp within that bin. The
+//     2048-bin histogram linear in key value over the unit's key range (the
+//     score step publishes each of its workgroups' minimum and maximum), built
+//     as the keys arrive, locates the pivot's bin; its keys (at most
+//     CAND_MAX) are ranked exactly by one wave, a fuller bin falls back to an
+//     8-pass radix select over comp within that bin. The
 //     sizes, block offsets and estimation logits of the workgroup's first
 //     512 own clusters are loaded at kernel start, behind the selection.
 //  2. Own clusters, 512 at a time: one block scan gives each retrieved
@@ -46,6 +48,7 @@
 //     out = sum_w e^{m_w-M} acc_w / sum_w e^{m_w-M} l_w.
 // Every sum runs in a fixed order, so results are bit-reproducible.
 #include <climits>
+#include <type_traits>
 
 #include "wi_internal.h"
 
@@ -71,6 +74,7 @@ static_assert(NT == 512 && BPT == 4 && KPT % 4 == 0, "thread layout");
 struct FusedArgs {
   const uint32_t* key;     // [U][Cp] order-preserving ranking keys
   const float* S;          // [U][C][GS] scaled per-head logits
+  const float2* mm;        // [U][NB] key ranges of the score workgroups
   const int32_t* size;     // [U][C]
   const int32_t* block_off;  // [U][C+1]
   const void* kblk;
@@ -83,7 +87,7 @@ struct FusedArgs {
   float* part;             // [U][W][G][PART]
   int* tix;                // [U] arrival counters, zero on entry
   uint8_t* zone;           // nullable: [U][C] 1 = retrieval, 2 = estimation
-  int C, Cp, n_st, G, H, Hq, K_r, K_e, W, lgT;
+  int C, Cp, n_st, G, H, Hq, K_r, K_e, W, lgT, NB;
   int64_t capT;
   float scale;
 };
@@ -173,8 +177,7 @@ __device__ __forceinline__ float ex(float x) {
 template <int GS>
 struct Lds {
   static constexpr int KEYS = 0;                              // uint32[CL]
-  static constexpr int BINS = KEYS + CL * 4;                  // uint16[CL]
-  static constexpr int HIST = BINS + CL * 2;                  // int[NBINS]
+  static constexpr int HIST = KEYS + CL * 4;                  // int[NBINS]
   static constexpr int CANDK = HIST + NBINS * 4;              // uint32[2][CAND_MAX]
   static constexpr int CANDI = CANDK + 2 * CAND_MAX * 4;      // int[2][CAND_MAX]
   static constexpr int RTOK = CANDI + 2 * CAND_MAX * 4;       // int[NT + 4]
@@ -191,7 +194,11 @@ struct Lds {
   static_assert(RTOK % 16 == 0 && PBUF % 16 == 0 && QS % 16 == 0, "align");
 };
 
-template <int DT, int GS>
+// BIG: more than CL clusters per unit (keys staged in several LDS passes).
+// Kept a separate instantiation so that the common kernel holds no
+// re-staging loads, after which the compiler would place waits for
+// outstanding loads.
+template <int DT, int GS, bool BIG>
 __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   using L = Lds<GS>;
   constexpr int NTILE = DT == WI_BF16 ? 2 : 1;  // 16-token MFMA tiles per wave block
@@ -201,7 +208,6 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   static_assert(PI <= PI_MAX, "weights buffer");
   __shared__ __align__(16) uint8_t smem[L::BYTES];
   uint32_t* keys = reinterpret_cast<uint32_t*>(smem + L::KEYS);
-  uint16_t* binl = reinterpret_cast<uint16_t*>(smem + L::BINS);
   int* hist = reinterpret_cast<int*>(smem + L::HIST);
   uint32_t* candk = reinterpret_cast<uint32_t*>(smem + L::CANDK);
   int* candi = reinterpret_cast<int*>(smem + L::CANDI);
@@ -213,7 +219,6 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   float* Pbuf = reinterpret_cast<float*>(smem + L::PBUF);
   uint8_t* qs = smem + L::QS;
   __shared__ int scan_lds[4 * NW];
-  __shared__ float redf[2][NW];
   __shared__ float wm[NW][MAX_G], wl[NW][MAX_G];
   __shared__ int bsel[2], bneed[2], ncand[2];
   __shared__ uint32_t pk[2];
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   const int r16 = lane & 15, kg = lane >> 4;
   const int C = a.C, G = a.G, W = a.W;
   const int K_r = a.K_r, K_e = a.K_e;
-  const int NP = (C + CL - 1) / CL;  // LDS passes over the keys
+  const int NP = BIG ? (C + CL - 1) / CL : 1;  // LDS passes over the keys
   const uint32_t* keyg = a.key + (int64_t)u * a.Cp;  // 16-byte aligned rows
   const int64_t uC = (int64_t)u * C;
   const int s_lo = (int)((int64_t)a.n_st * w / W), s_hi = (int)((int64_t)a.n_st * (w + 1) / W);
@@ -263,77 +268,65 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     for (int g4 = 0; g4 < GS / 4; g4++) sl0[g4] = sp[g4];
   }
 
-  // ---- stage keys [p CL, p CL + n) into LDS (ends with a barrier) -----------
-  float lo = INFINITY, hi = -INFINITY;
-  auto stage = [&](int p) {
+  // ---- keys of pass p (ids [p CL, p CL + n)): loads, then LDS stores -------
+  auto stage_load = [&](int p, uint4* k4) {
     const int c0 = p * CL, n = min(CL, C - c0);
-    uint4 k4[KPT / 4];
 #pragma unroll
     for (int r = 0; r < KPT / 4; r++) {
       const int i = 4 * (tid + r * NT);
       // rows are padded to a multiple of 4 keys: a load at i < n stays in the row
       k4[r] = i < n ? *reinterpret_cast<const uint4*>(keyg + c0 + i) : make_uint4(0u, 0u, 0u, 0u);
     }
-#pragma unroll
-    for (int r = 0; r < KPT / 4; r++) {
-      const int i = 4 * (tid + r * NT);
-      if (i < n) {
-        *reinterpret_cast<uint4*>(keys + i) = k4[r];
-        const uint32_t kk[4] = {k4[r].x, k4[r].y, k4[r].z, k4[r].w};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const float f = key_value(kk[e]);
-          lo = i + e < n ? fminf(lo, f) : lo;
-          hi = i + e < n ? fmaxf(hi, f) : hi;
-        }
-      }
-    }
-    __syncthreads();
   };
-
-  // ---- 1a. value range ------------------------------------------------------
-  for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
-  if (tid < 2) ncand[tid] = 0;
-  for (int p = 0; p < NP; p++) {
-    if (p > 0) __syncthreads();
-    stage(p);
-  }
-  lo = -wave_max_u(-lo);
-  hi = wave_max_u(hi);
-  if (lane == 0) {
-    redf[0][wv] = lo;
-    redf[1][wv] = hi;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NW; i++) {
-    lo = fminf(lo, redf[0][i]);
-    hi = fmaxf(hi, redf[1][i]);
-  }
-  const float inv = hi > lo ? (float)NBINS / (hi - lo) : 0.f;
-
-  // ---- 1b. histogram (bins also kept in LDS) --------------------------------
-  for (int p = 0; p < NP; p++) {
-    if (NP > 1) {
-      __syncthreads();
-      stage(p);
-    }
+  float lo = INFINITY, hi = -INFINITY, inv = 0.f;
+  auto stage_store = [&](int p, const uint4* k4, bool count) {
     const int n = min(CL, C - p * CL);
 #pragma unroll
     for (int r = 0; r < KPT / 4; r++) {
       const int i = 4 * (tid + r * NT);
       if (i < n) {
-        const uint4 k4 = *reinterpret_cast<const uint4*>(keys + i);
-        const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
-        int bn[4];
+        *reinterpret_cast<uint4*>(keys + i) = k4[r];
+        if (count) {
+          const uint32_t kk[4] = {k4[r].x, k4[r].y, k4[r].z, k4[r].w};
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          bn[e] = bin_of(kk[e], lo, inv);
-          if (i + e < n) atomicAdd(&hist[bn[e]], 1);
+          for (int e = 0; e < 4; e++)
+            if (i + e < n) atomicAdd(&hist[bin_of(kk[e], lo, inv)], 1);
         }
-        *reinterpret_cast<uint2*>(binl + i) = make_uint2(
-            (uint32_t)bn[0] | ((uint32_t)bn[1] << 16), (uint32_t)bn[2] | ((uint32_t)bn[3] << 16));
       }
+    }
+  };
+  // re-stage pass p for a later scan (C > CL only); leaves keys ready in LDS
+  auto restage = [&](int p) {
+    uint4 k4[KPT / 4];
+    __syncthreads();
+    stage_load(p, k4);
+    stage_store(p, k4, false);
+    __syncthreads();
+  };
+
+  // ---- 1a.-1b. key range (from the score step) and histogram -----------------
+  for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+  if (tid < 2) ncand[tid] = 0;
+  {
+    uint4 k4[KPT / 4];
+    stage_load(0, k4);
+    // every wave reduces the score workgroups' ranges the same way
+    const float2* mmu = a.mm + (int64_t)u * a.NB;
+#pragma unroll 1
+    for (int j = lane; j < a.NB; j += 64) {
+      const float2 r = mmu[j];
+      lo = fminf(lo, r.x);
+      hi = fmaxf(hi, r.y);
+    }
+    lo = -wave_max_u(-lo);
+    hi = wave_max_u(hi);
+    inv = hi > lo ? (float)NBINS / (hi - lo) : 0.f;
+    __syncthreads();  // histogram cleared
+    stage_store(0, k4, true);
+#pragma unroll 1
+    for (int p = 1; p < NP; p++) {
+      stage_load(p, k4);
+      stage_store(p, k4, true);
     }
   }
   __syncthreads();
@@ -370,33 +363,75 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   __syncthreads();
   const int b1 = need0 ? bsel[0] : -1, b2 = need1 ? bsel[1] : -1;
 
-  // ---- 1d. keys of the pivot bins -------------------------------------------
-  for (int p = 0; p < NP; p++) {
-    if (NP > 1) {
-      __syncthreads();
-      stage(p);
-      const int n = min(CL, C - p * CL);
-      for (int i = 4 * tid; i < n; i += 4 * NT) {
-        const uint4 k4 = *reinterpret_cast<const uint4*>(keys + i);
-        *reinterpret_cast<uint2*>(binl + i) =
-            make_uint2((uint32_t)bin_of(k4.x, lo, inv) | ((uint32_t)bin_of(k4.y, lo, inv) << 16),
-                       (uint32_t)bin_of(k4.z, lo, inv) | ((uint32_t)bin_of(k4.w, lo, inv) << 16));
-      }
-      __syncthreads();
+  // ---- warm the L2 with the data the first chunk will most likely read -------
+  // Once the pivot bins are known, an own cluster in a bin at or above the
+  // retrieval pivot's bin may be retrieved, one at or above the estimation
+  // pivot's bin may be selected. Their value sums (thread per cluster, one
+  // dword per 128-byte line) and key/value rows (wave per cluster, first
+  // 4 KB of each) are requested now, while the selection finishes; the
+  // loaded words are only folded together at the end of the kernel, so
+  // nothing waits for them.
+  constexpr int RB = D * (DT == WI_BF16 ? 2 : 4);  // bytes per K/V row
+  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(a.kblk) + (int64_t)u * a.capT * RB;
+  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(a.vblk) + (int64_t)u * a.capT * RB;
+  const uint8_t* sk8 = reinterpret_cast<const uint8_t*>(a.stk) + (int64_t)u * a.n_st * RB;
+  const uint8_t* sv8 = reinterpret_cast<const uint8_t*>(a.stv) + (int64_t)u * a.n_st * RB;
+  // a valid row of at least RB bytes, read by lanes without an item
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.vsum + uC * D);
+  const int lgT = a.lgT;
+  // kept apart until the end so that no instruction waits for them
+  uint32_t w4[4] = {0u, 0u, 0u, 0u}, wk[4] = {0u, 0u, 0u, 0u}, wst = 0u;
+  {
+    const int id0 = own_id(tid);
+    const bool ok = tid < n_own && id0 < C && sz0 > 0;
+    const int bn = ok ? bin_of(NP == 1 ? keys[id0] : keyg[id0], lo, inv) : -1;
+    const bool maybeS = ok && (M1 >= C || (need1 && bn >= b2));
+    const bool maybeR = ok && (M0 >= C || (need0 && bn >= b1));
+    const bool surelyR = ok && (M0 >= C || (need0 && bn > b1));
+    if (maybeS && !surelyR) {
+      const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.vsum + (uC + id0) * D);
+#pragma unroll
+      for (int j = 0; j < 4; j++) w4[j] = vp[32 * j];
     }
+    // up to 4 retrieval candidates per wave; lanes 0-31 read the key rows,
+    // 32-63 the value rows, one 128-byte line each
+    uint64_t cand = __ballot(maybeR);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      if (cand) {
+        const int l = __builtin_ctzll(cand);
+        cand &= cand - 1;
+        const int cb = rdl(blk0, l), cn = rdl(sz0, l);
+        const int off = (lane & 31) * 128;
+        if (off < cn * RB)
+          wk[c] = *reinterpret_cast<const uint32_t*>((lane < 32 ? kb8 : vb8) +
+                                                     ((int64_t)cb << lgT) * RB + off);
+      }
+    }
+    // the steady rows of this workgroup (wave 0)
+    if (wv == 0) {
+      const int off = (lane & 31) * 128;
+      if (off < (s_hi - s_lo) * RB)
+        wst = *reinterpret_cast<const uint32_t*>((lane < 32 ? sk8 : sv8) +
+                                                   (int64_t)s_lo * RB + off);
+    }
+  }
+
+  // ---- 1d. keys of the pivot bins -------------------------------------------
+  auto cand_scan = [&](int p) {
     const int n = min(CL, C - p * CL);
 #pragma unroll
     for (int r = 0; r < KPT / 4; r++) {
       const int i = 4 * (tid + r * NT);
       if (i >= n) continue;
-      const uint2 b4 = *reinterpret_cast<const uint2*>(binl + i);
-      const int bns[4] = {(int)(b4.x & 0xFFFFu), (int)(b4.x >> 16), (int)(b4.y & 0xFFFFu),
-                          (int)(b4.y >> 16)};
+      const uint4 k4 = *reinterpret_cast<const uint4*>(keys + i);
+      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+      int bns[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) bns[e] = bin_of(kk[e], lo, inv);
       const bool any = (bns[0] == b1) | (bns[1] == b1) | (bns[2] == b1) | (bns[3] == b1) |
                        (bns[0] == b2) | (bns[1] == b2) | (bns[2] == b2) | (bns[3] == b2);
       if (!any) continue;
-      const uint4 k4 = *reinterpret_cast<const uint4*>(keys + i);
-      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         if (i + e < n) {
@@ -412,6 +447,17 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
           }
         }
       }
+    }
+  };
+  // (two code paths, so that the common one issues no global load and the
+  // compiler puts no wait for outstanding loads in it)
+  if (NP == 1) {
+    cand_scan(0);
+  } else {
+#pragma unroll 1
+    for (int p = 0; p < NP; p++) {
+      restage(p);
+      cand_scan(p);
     }
   }
   __syncthreads();
@@ -454,7 +500,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
         for (int i = tid; i < 256; i += NT) rdx[i] = 0;
         __syncthreads();
         for (int p = 0; p < NP; p++) {
-          if (NP > 1) stage(p);
+          if (NP > 1) restage(p);
           const int n = min(CL, C - p * CL);
 #pragma unroll 1
           for (int i = tid; i < n; i += NT) {
@@ -465,7 +511,6 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
                 atomicAdd(&rdx[(comp >> shift) & 255], 1);
             }
           }
-          if (NP > 1) __syncthreads();
         }
         __syncthreads();
         if (tid == 0) {
@@ -495,14 +540,6 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   const bool noneR = M0 <= 0, noneS = M1 <= 0;
 
   // ---- 2.-3. own clusters, NT at a time, then their items --------------------
-  constexpr int RB = D * (DT == WI_BF16 ? 2 : 4);  // bytes per K/V row
-  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(a.kblk) + (int64_t)u * a.capT * RB;
-  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(a.vblk) + (int64_t)u * a.capT * RB;
-  const uint8_t* sk8 = reinterpret_cast<const uint8_t*>(a.stk) + (int64_t)u * a.n_st * RB;
-  const uint8_t* sv8 = reinterpret_cast<const uint8_t*>(a.stv) + (int64_t)u * a.n_st * RB;
-  // a valid row of at least RB bytes, read by lanes without an item
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.vsum + uC * D);
-  const int lgT = a.lgT;
   float* pb = Pbuf + wv * PI_MAX * GS;  // this wave's weights p[item][head]
 
   // Online softmax state of this wave. Lanes of column r16 (r16, r16 + 16,
@@ -514,61 +551,73 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
 #pragma unroll
   for (int g = 0; g < GS; g++) acc[g][0] = acc[g][1] = 0.f;
 
-#pragma unroll 1
-  for (int ch = 0; ch < n_chunks; ch++) {
-    // (i) zones of the chunk's clusters and the chunk's item lists
-    const int k = ch * NT + tid;
-    const int id = own_id(k);
-    const bool ok = k < n_own && id < C;
-    const int idc = ok ? id : 0;
-    int n, blk;
-    f32x4_t sl[GS / 4];
-    const uint32_t kk = NP == 1 ? keys[idc] : keyg[idc];
-    if (ch == 0) {
-      n = sz0;
-      blk = blk0;
+  // one chunk of own clusters; the first is peeled off the loop, so that its
+  // code joins no path holding later chunks' loads (the compiler would
+  // otherwise place waits there that also cover the warm-up loads)
+  auto chunk = [&](const int ch) {
+    // (i) zones of the chunk's clusters and the chunk's item lists. The
+    // first chunk's cluster data was loaded at kernel start; a later chunk
+    // loads its own inside its branch. Each branch consumes what it loads,
+    // so the compiler places no wait for other outstanding loads after it.
+    int nR = 0, nRtok = 0, nE = 0;
+    auto setup = [&](int n, int blk, const f32x4_t* sl) {
+      const int k = ch * NT + tid;
+      const int id = own_id(k);
+      const bool ok = k < n_own && id < C;
+      const int idc = ok ? id : 0;
+      const uint32_t kk = NP == 1 ? keys[idc] : keyg[idc];
+      const uint64_t comp = comp_of(kk, id);
+      const bool inS = ok && !noneS && comp >= cS;
+      const bool inR = inS && !noneR && comp >= cR;
+      const bool inE = inS && !inR;
+      if (a.zone && ok) a.zone[uC + id] = inR ? 1 : (inE ? 2 : 0);
+      const bool rT = inR && n > 0, eT = inE && n > 0;  // zones with members
+      const int v3[3] = {(int)rT, rT ? n : 0, (int)eT};
+      int off3[3], tot3[3];
+      block_scan<3>(v3, off3, tot3, scan_lds);
+      nR = tot3[0];
+      nRtok = tot3[1];
+      nE = tot3[2];
+      if (rT) {
+        Rtok[off3[0]] = off3[1];
+        Rblk[off3[0]] = blk;
+      }
+      if (eT) {
+        Eid[off3[2]] = id;
+        Esz[off3[2]] = (float)n;
+        float* el = Elog + off3[2] * GS;
 #pragma unroll
-      for (int g4 = 0; g4 < GS / 4; g4++) sl[g4] = sl0[g4];
+        for (int g4 = 0; g4 < GS / 4; g4++) *reinterpret_cast<f32x4_t*>(el + 4 * g4) = sl[g4];
+      }
+    };
+    if (ch == 0) {
+      setup(sz0, blk0, sl0);
     } else {
-      n = a.size[uC + idc];
-      blk = a.block_off[(int64_t)u * (C + 1) + idc];
+      const int k = ch * NT + tid;
+      const int id = own_id(k);
+      const int idc = k < n_own && id < C ? id : 0;
+      const int n = a.size[uC + idc];
+      const int blk = a.block_off[(int64_t)u * (C + 1) + idc];
+      f32x4_t sl[GS / 4];
       const f32x4_t* sp = reinterpret_cast<const f32x4_t*>(a.S + (uC + idc) * GS);
 #pragma unroll
       for (int g4 = 0; g4 < GS / 4; g4++) sl[g4] = sp[g4];
-    }
-    const uint64_t comp = comp_of(kk, id);
-    const bool inS = ok && !noneS && comp >= cS;
-    const bool inR = inS && !noneR && comp >= cR;
-    const bool inE = inS && !inR;
-    if (a.zone && ok) a.zone[uC + id] = inR ? 1 : (inE ? 2 : 0);
-    const bool rT = inR && n > 0, eT = inE && n > 0;  // zones with members
-    const int v3[3] = {(int)rT, rT ? n : 0, (int)eT};
-    int off3[3], tot3[3];
-    block_scan<3>(v3, off3, tot3, scan_lds);
-    const int nR = tot3[0], nRtok = tot3[1], nE = tot3[2];
-    if (rT) {
-      Rtok[off3[0]] = off3[1];
-      Rblk[off3[0]] = blk;
-    }
-    if (eT) {
-      Eid[off3[2]] = id;
-      Esz[off3[2]] = (float)n;
-      float* el = Elog + off3[2] * GS;
-#pragma unroll
-      for (int g4 = 0; g4 < GS / 4; g4++) *reinterpret_cast<f32x4_t*>(el + 4 * g4) = sl[g4];
+      setup(n, blk, sl);
     }
     __syncthreads();
     // token items: the own steady tokens (first chunk only), then the chunk's
     // retrieved tokens; estimation items: the chunk's estimation clusters.
-    // Wave wv takes blocks wv, wv + NW, ... of TB tokens and EB clusters.
+    // Wave wv takes token blocks (TB tokens) wv, wv + NW, ... and estimation
+    // blocks (EB clusters) NW - 1 - wv, 2 NW - 1 - wv, ..., so that small
+    // chunks spread both kinds of work over all waves.
     const int nS = ch == 0 ? s_hi - s_lo : 0;
     const int nT = nS + nRtok;
-    const int nB = max((nT + TB - 1) / TB, (nE + EB - 1) / EB);
+    const int nTB = (nT + TB - 1) / TB, nEB = (nE + EB - 1) / EB;
     const int s0 = nR > 1 ? 1 << (31 - __clz(nR - 1)) : 0;  // binary-search stride
 
 #pragma unroll 1
-    for (int bk = wv; bk < nB; bk += NW) {
-      const int t0 = bk * TB, e0 = bk * EB;
+    for (int it = 0; wv + it * NW < nTB || NW - 1 - wv + it * NW < nEB; it++) {
+      const int t0 = (wv + it * NW) * TB, e0 = (NW - 1 - wv + it * NW) * EB;
       const int ntw = max(0, min(TB, nT - t0)), new_ = max(0, min(EB, nE - e0));
       // (a) rows: lane r16 of tile j holds token item t0 + 16 j + r16 (steady
       // row, or a slot of its retrieved cluster found by binary search)
@@ -749,7 +798,14 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-  }
+  };
+  chunk(0);
+#pragma unroll 1
+  for (int ch = 1; ch < n_chunks; ch++) chunk(ch);
+
+  // the warm-up values are consumed (the condition never holds: K_r >= 0)
+  const uint32_t warm = w4[0] ^ w4[1] ^ w4[2] ^ w4[3] ^ wk[0] ^ wk[1] ^ wk[2] ^ wk[3] ^ wst;
+  if (warm == 0x9E3779B9u && K_r < 0) a.out[0] = 0.f;
 
   // ---- 4. merge the waves (fixed order), publish, count arrivals --------------
   // each wave's denominator: its column's four lane shares
@@ -798,64 +854,76 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
 
   // ---- 5. the last workgroup of the unit merges the W partials -------------
   // A thread's accumulator loads for its first output element (one per
-  // partial, up to 64) are issued first, then the (m, l) of every partial; the
+  // partial; NV = 16, 32 or 64 >= W slots, slots v >= W repeat partial W - 1
+  // and get weight 0) are issued first, then the (m, l) of every partial; the
   // weights e^{m_w - M} and the denominators are formed on chip. Every thread
   // reaches both barriers.
   const float* pu = a.part + (int64_t)u * W * G * PART;
   float* cm = reinterpret_cast<float*>(smem);  // [W][G] m
-  float* cl = cm + 64 * MAX_G;                 // [W][G] l, then weights
-  // slots v >= W repeat partial W - 1 and get weight 0
-  auto acc_loads = [&](int e, float av[MAX_WG]) {
-    const int g = e >> 7, t = e & (D - 1);
+  float* cl = cm + MAX_WG * MAX_G;             // [MAX_WG][G] l, then weights
+  auto combine = [&](auto nv) {
+    constexpr int NV = decltype(nv)::value;
+    auto acc_loads = [&](int e, float* av) {
+      const int g = e >> 7, t = e & (D - 1);
 #pragma unroll
-    for (int v = 0; v < MAX_WG; v++)
-      av[v] = __hip_atomic_load(pu + ((int64_t)min(v, W - 1) * G + g) * PART + 2 + t,
-                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto finish = [&](int e, const float av[MAX_WG]) {
-    const int g = e >> 7, t = e & (D - 1);
-    float num = 0.f;
+      for (int v = 0; v < NV; v++)
+        av[v] = __hip_atomic_load(pu + ((int64_t)min(v, W - 1) * G + g) * PART + 2 + t,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto finish = [&](int e, const float* av) {
+      const int g = e >> 7, t = e & (D - 1);
+      float num = 0.f;
 #pragma unroll
-    for (int v = 0; v < MAX_WG; v++) num = fmaf(cl[v * G + g], av[v], num);
-    const float den = cden[g];
-    a.out[((int64_t)b * a.Hq + (int64_t)h * G + g) * D + t] = den > 0.f ? num / den : 0.f;
+      for (int v = 0; v < NV; v++) num = fmaf(cl[v * G + g], av[v], num);
+      const float den = cden[g];
+      a.out[((int64_t)b * a.Hq + (int64_t)h * G + g) * D + t] = den > 0.f ? num / den : 0.f;
+    };
+    float av[NV];
+    const bool has = tid < G * D;
+    if (has) acc_loads(tid, av);
+    for (int i = tid; i < W * G; i += NT) {
+      cm[i] = __hip_atomic_load(pu + (int64_t)i * PART, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+      cl[i] = __hip_atomic_load(pu + (int64_t)i * PART + 1, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    // wave g handles head g, lane v partial v (W <= MAX_WG = 64)
+#pragma unroll 1
+    for (int g = wv; g < G; g += NW) {
+      const float mv = lane < W ? cm[lane * G + g] : -INFINITY;
+      const float M2 = wave_max_u(mv);
+      const float f = (mv == -INFINITY) ? 0.f : ex<DT>(mv - M2);
+      const float lv = lane < W ? cl[lane * G + g] : 0.f;
+      const float den = wave_sum_u(f * lv);
+      cl[lane * G + g] = lane < W ? f : 0.f;  // weight
+      if (lane == 0) cden[g] = den;
+    }
+    __syncthreads();
+    if (has) finish(tid, av);
+#pragma unroll 1
+    for (int e = tid + NT; e < GS * D && e < G * D; e += NT) {
+      acc_loads(e, av);
+      finish(e, av);
+    }
   };
-  float av[MAX_WG];
-  const bool has = tid < G * D;
-  if (has) acc_loads(tid, av);
-  for (int i = tid; i < W * G; i += NT) {
-    cm[i] = __hip_atomic_load(pu + (int64_t)i * PART, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    cl[i] = __hip_atomic_load(pu + (int64_t)i * PART + 1, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  // wave g handles head g, lane v partial v (W <= MAX_WG = 64)
-#pragma unroll 1
-  for (int g = wv; g < G; g += NW) {
-    const float mv = lane < W ? cm[lane * G + g] : -INFINITY;
-    const float M2 = wave_max_u(mv);
-    const float f = (mv == -INFINITY) ? 0.f : ex<DT>(mv - M2);
-    const float lv = lane < W ? cl[lane * G + g] : 0.f;
-    const float den = wave_sum_u(f * lv);
-    cl[lane * G + g] = lane < W ? f : 0.f;  // weight
-    if (lane == 0) cden[g] = den;
-  }
-  __syncthreads();
-  if (has) finish(tid, av);
-#pragma unroll 1
-  for (int e = tid + NT; e < GS * D && e < G * D; e += NT) {
-    acc_loads(e, av);
-    finish(e, av);
-  }
+  if (W <= 16) combine(std::integral_constant<int, 16>{});
+  else if (W <= 32) combine(std::integral_constant<int, 32>{});
+  else combine(std::integral_constant<int, MAX_WG>{});
+}
+
+template <int DT, bool BIG>
+hipError_t launch_fused_big(const DecodeArgs& da, const FusedArgs& fa, hipStream_t s) {
+  dim3 grid(da.W, da.g->U);
+  if (da.GS == 4) WI_LAUNCH(K_FUSED, (fused_kernel<DT, 4, BIG>), grid, dim3(NT), 0, s, fa);
+  else if (da.GS == 8) WI_LAUNCH(K_FUSED, (fused_kernel<DT, 8, BIG>), grid, dim3(NT), 0, s, fa);
+  else WI_LAUNCH(K_FUSED, (fused_kernel<DT, 16, BIG>), grid, dim3(NT), 0, s, fa);
+  return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_fused_dt(const DecodeArgs& da, const FusedArgs& fa, hipStream_t s) {
-  dim3 grid(da.W, da.g->U);
-  if (da.GS == 4) WI_LAUNCH(K_FUSED, (fused_kernel<DT, 4>), grid, dim3(NT), 0, s, fa);
-  else if (da.GS == 8) WI_LAUNCH(K_FUSED, (fused_kernel<DT, 8>), grid, dim3(NT), 0, s, fa);
-  else WI_LAUNCH(K_FUSED, (fused_kernel<DT, 16>), grid, dim3(NT), 0, s, fa);
-  return hipGetLastError();
+  return fa.C > CL ? launch_fused_big<DT, true>(da, fa, s) : launch_fused_big<DT, false>(da, fa, s);
 }
 
 }  // namespace
@@ -866,6 +934,8 @@ hipError_t launch_fused(const DecodeArgs& da, const wi_index_bufs& bf, const voi
   FusedArgs fa;
   fa.key = ws.key;
   fa.S = ws.S;
+  fa.mm = ws.mm;
+  fa.NB = score_blocks(g);
   fa.size = bf.cluster_size;
   fa.block_off = bf.block_off;
   fa.kblk = bf.k_blocks;

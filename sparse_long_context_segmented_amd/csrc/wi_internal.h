@@ -79,6 +79,7 @@ constexpr int KPP_SLICE = 256;  // points per k-means++ workgroup
 struct DecodeWs {
   uint32_t* key;       // [U][Cp] order-preserving ranking keys (Cp = C rounded up to 4)
   float* S;            // [U*C*GS] scaled per-head centroid logits (GS = 4, 8, 16)
+  float2* mm;          // [U][score_blocks] key range (min, max) of each score workgroup
   float* part;         // [U*W*G*(2+128)] per-workgroup partials (m, l, acc)
   int* tix;            // [U] arrival counters of the fused kernel
   uint8_t* zone;       // [U*C] 1 retrieval, 2 estimation, 0 neither (debug outputs only)
@@ -221,6 +222,7 @@ struct DecodeArgs {
   int W;                    // fused-kernel workgroups per unit (<= MAX_WG)
   float scale;
 };
+int score_blocks(const Geom& g);  // score-kernel workgroups per unit
 hipError_t launch_score(const DecodeArgs& a, const void* centroids, const void* q,
                         const DecodeWs& ws, hipStream_t s);
 hipError_t launch_fused(const DecodeArgs& a, const wi_index_bufs& b, const void* q,
