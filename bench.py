@@ -29,6 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_llama8b_128k_b1_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_long_context_segmented_amd", "csrc", f)
+                  for f in ("decode_fused.hip", "decode_score.hip", "wi_internal.h")]
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 
@@ -50,6 +53,26 @@ def parse():
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3 (no CPU leg, few steps)")
     return ap.parse_args()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the select/attend kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a copy kernel), or
+    None when that summary is for another workload or for other kernel
+    sources than the ones built here."""
+    if workload != "llama8b-128k-b1" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    import hashlib
+    line = [x for x in open(TRAFFIC_PROFILE) if x.startswith("traffic: ")]
+    if not line:
+        return None
+    rec = json.loads(line[0][len("traffic: "):])
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    if h.hexdigest()[:16] != rec.get("sources_sha256"):
+        return None
+    return int(rec["bytes"])
 
 
 def main():
@@ -175,7 +198,7 @@ def main():
     achieved = dom_bytes / (avg[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(w.name),
                 "kernel_ms": {k: round(v, 5) for k, v in avg.items()},
                 "algorithmic_bytes": {k: int(v) for k, v in per_kernel.items()}}
 
