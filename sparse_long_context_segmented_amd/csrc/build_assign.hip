@@ -7,20 +7,31 @@
 // in dimension order, lowest centroid id on ties. It is computed in two
 // stages:
 //
-// 1. MFMA stage (dense contraction). The score s_c = 2<x, mu_c> - |mu_c|^2
-//    (argmax s_c = argmin distance) of a 256-point tile against all
-//    centroids of its segment: centroids are the A operand (rows), staged in
-//    LDS 256 at a time, pre-doubled (exact) with 16-byte row padding; points
-//    are the B operand (columns) held in registers for the whole sweep.
-//    bf16 uses v_mfma_f32_32x32x16_bf16 (products exact, fp32
-//    accumulation); fp32 uses v_mfma_f32_32x32x2_f32. The epilogue keeps,
-//    per point, the best score, its centroid and the second-best score.
-// 2. Certification. With |s~ - s| <= gamma_130 (|x|^2 + 2 max_c |mu_c|^2)
-//    for either accumulation, a point whose best score leads the second by
-//    more than W = 2^-12 (|x|^2 + 2 max|mu|^2) -- at least 15x that bound,
-//    doubled -- has its exact nearest centroid at the MFMA winner. Other
-//    points are listed and the fallback kernel evaluates the exact float64
-//    distance to every centroid of their segment.
+// 1. MFMA stage (dense contraction). bf16: a workgroup of 512 points stages
+//    all (<= 512) centroids of its segment in LDS once; each wave holds 64
+//    points as the B operand (columns) and sweeps 32-centroid row tiles with
+//    v_mfma_f32_32x32x16_bf16 (products exact, fp32 accumulation). One extra
+//    k-step of 16 folds two constants into the contraction, each split
+//    exactly into three bf16 parts: -|mu_c|^2 / 2 (A side, times 1 on B) and
+//    off_p / 2 (B side, times 1 on A), off_p = (|x_p|^2 + 2 max_c |mu_c|^2)
+//    (1 + 2^-10) + 1. The accumulator is then a_pc = (s_pc + off_p) / 2 with
+//    s_pc = 2<x, mu_c> - |mu_c|^2 (argmax s = argmin distance), and a_pc > 0.
+//    Its low 9 mantissa bits are replaced by 511 - c, so an unsigned max
+//    keeps the best (lowest c on equal high bits) and an unsigned median
+//    the second best: three integer ops per score.
+//    fp32 (parity-size workloads) keeps a plain epilogue over
+//    v_mfma_f32_32x32x2_f32 with the centroids staged 128 at a time.
+// 2. Certification. An encoded value lies within (a - e - 2^-14 off, a + e]
+//    of its exact a, with e <= gamma_144 * 1.25 off < 2^-16.3 off (fp32
+//    accumulation of <= 144 terms whose magnitudes sum to <= 1.25 off) and
+//    2^-14 off for the dropped bits. If another centroid held the top
+//    encoded value, the lead over the second would be at most
+//    2e + 2^-14 off < 2^-13 off; so a point whose best encoded value leads
+//    the second by more than 2^-13 off has its exact nearest centroid at the
+//    encoded winner (fp32: the previous bound, lead over 2^-12
+//    (|x|^2 + 2 max|mu|^2) on s). Other points are listed and the fallback
+//    kernel evaluates the exact float64 distance to every centroid of their
+//    segment.
 #include "wi_internal.h"
 
 namespace wi {
@@ -69,36 +80,117 @@ __device__ __forceinline__ Best merge(Best a, Best o) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16: each wave owns 2 column tiles of 32 points (64 points per wave).
-__global__ __launch_bounds__(AT, 2) void assign_bf16_kernel(Geom g, const void* __restrict__ K,
+// bf16: 8 waves x 64 points (2 column tiles of 32) per workgroup.
+constexpr int BT = 512;                  // threads per workgroup
+constexpr int ROWA = D * 2 + 16;         // LDS centroid row (bf16, padded)
+constexpr size_t BF16_LDS = (size_t)MAX_K * ROWA + MAX_K * 16 + 64;
+constexpr uint32_t BF1 = 0x3F80u;        // bf16 1.0
+
+// x = h1 + h2 + h3 exactly up to rounding of the last part (bf16 bits)
+__device__ __forceinline__ void split3(float x, uint32_t& h1, uint32_t& h2, uint32_t& h3) {
+  const float a = __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
+  const float r = x - a;
+  const float b = __uint_as_float(__float_as_uint(r) & 0xFFFF0000u);
+  const float c = r - b;
+  h1 = __float_as_uint(a) >> 16;
+  h2 = __float_as_uint(b) >> 16;
+  h3 = f32_to_bf16_rne(c);
+}
+
+// Workgroup (blockIdx.x, segment) handles the segment's 512-point blocks
+// blockIdx.x, blockIdx.x + gridDim.x, ...: the centroids are staged once, and
+// the next block's points are loaded during the current block's MFMA sweep.
+__global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* __restrict__ K,
                                                             const void* __restrict__ cent,
                                                             BuildWs ws) {
   constexpr int NTL = 2;
   extern __shared__ __align__(16) uint8_t lds[];
-  uint8_t* crow = lds;                                         // CHUNK rows of ROWB
-  float* cnorm = reinterpret_cast<float*>(lds + CHUNK * ROWB);  // CHUNK norms
-  float* red = cnorm + CHUNK;                                   // 4 floats
+  uint8_t* crow = lds;                                                  // MAX_K rows
+  uint4* ctail = reinterpret_cast<uint4*>(lds + (size_t)MAX_K * ROWA);  // A tail, k 0..7
+  float* red = reinterpret_cast<float*>(ctail + MAX_K);                 // 8 floats
 
   const int gs = blockIdx.y, u = gs / g.n_seg, s = gs % g.n_seg;
   const int n = seg_n(g, s), Cs = seg_c(g, s), cb = seg_cbase(g, s);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int p0 = blockIdx.x * 256;  // 4 waves x 64 points
-  if (p0 >= n) return;
+  if (blockIdx.x * BT >= n) return;
   const int64_t first = seg_first(g, s);
+  // rows staged: a multiple of 64 (pairs of 32-row tiles); rows past Cs are
+  // zero, tail included, so their scores are 0 and never win
+  const int Cp = (Cs + 63) & ~63;
 
-  // B fragments: point p = p0 + 64*wv + 32*t + (lane & 31), dims
-  // 16*k + 8*(lane >> 5) .. +8, for k = 0..7.
-  uint4 bfrag[NTL][8];
-  float xn[NTL];
+  // B fragments of a block: point p = p0 + 64 wv + 32 t + (lane & 31), dims
+  // 16 k + 8 (lane >> 5) .. + 8, for k = 0..7
+  auto load_points = [&](int p0, uint4 (*bf)[8]) {
 #pragma unroll
-  for (int t = 0; t < NTL; t++) {
-    const int p = p0 + 64 * wv + 32 * t + (lane & 31);
-    float sq = 0.f;
-    if (p < n) {
+    for (int t = 0; t < NTL; t++) {
+      const int p = min(p0 + 64 * wv + 32 * t + (lane & 31), n - 1);  // clamped; not written
       const uint4* row = reinterpret_cast<const uint4*>(kptr<WI_BF16>(K, g, u, first + p));
 #pragma unroll
+      for (int k = 0; k < 8; k++) bf[t][k] = row[2 * k + (lane >> 5)];
+    }
+  };
+  // the first block's points are requested before the centroids
+  uint4 bfrag[NTL][8];
+  load_points(blockIdx.x * BT, bfrag);
+  // stage the segment's centroids: 16 lanes per row, 16 bytes each, 32 rows
+  // per pass; |mu|^2 per row in float32 (fixed order), A tails from it
+  const uint16_t* C16 = reinterpret_cast<const uint16_t*>(cent) + ((int64_t)u * g.C + cb) * D;
+  float mmax = 0.f;
+  {
+    constexpr int PASSES = MAX_K / (BT / 16);  // 16
+    uint4 cv[PASSES];
+    const int j = tid & 15;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ps++) {
+      const int c = ps * (BT / 16) + (tid >> 4);
+      cv[ps] = c < Cs ? reinterpret_cast<const uint4*>(C16 + (int64_t)c * D)[j]
+                      : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ps++) {
+      const int c = ps * (BT / 16) + (tid >> 4);
+      if (c < Cp) {
+        *reinterpret_cast<uint4*>(crow + c * ROWA + 16 * j) = cv[ps];
+        const uint32_t w[4] = {cv[ps].x, cv[ps].y, cv[ps].z, cv[ps].w};
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float a = __uint_as_float(w[e] << 16), b2 = __uint_as_float(w[e] & 0xFFFF0000u);
+          sq = fmaf(a, a, sq);
+          sq = fmaf(b2, b2, sq);
+        }
+        sq = row16_sum(sq);  // the row's 16 lanes hold its 16 pieces
+        if (c < Cs) mmax = fmaxf(mmax, sq);
+        if (j == 0) {
+          uint32_t h1, h2, h3;
+          split3(0.5f * sq, h1, h2, h3);
+          // [-h1, -h2, -h3, 1, 1, 1, 0, 0] (k = 0..7); rows past Cs all zero
+          ctail[c] = c < Cs ? make_uint4((h1 ^ 0x8000u) | ((h2 ^ 0x8000u) << 16),
+                                         (h3 ^ 0x8000u) | (BF1 << 16), BF1 | (BF1 << 16), 0u)
+                            : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+  }
+  mmax = wave_max(mmax);
+  if (lane == 0) red[wv] = mmax;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < BT / 64; i++) mmax = fmaxf(mmax, red[i]);
+  const int nm = Cp / 32;
+
+#pragma unroll 1
+  for (int p0 = blockIdx.x * BT; p0 < n; p0 += gridDim.x * BT) {
+
+    // per point: |x|^2, the offset and the B tail [1, 1, 1, o1, o2, o3, 0, 0]
+    // (lanes 0-31 supply k = 0..7 of the extra step; lanes 32-63 zeros)
+    uint4 btail[NTL];
+    float offs[NTL];
+#pragma unroll
+    for (int t = 0; t < NTL; t++) {
+      float sq = 0.f;
+#pragma unroll
       for (int k = 0; k < 8; k++) {
-        bfrag[t][k] = row[2 * k + (lane >> 5)];
         const uint32_t w[4] = {bfrag[t][k].x, bfrag[t][k].y, bfrag[t][k].z, bfrag[t][k].w};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
@@ -107,102 +199,96 @@ __global__ __launch_bounds__(AT, 2) void assign_bf16_kernel(Geom g, const void* 
           sq = fmaf(b2, b2, sq);
         }
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; k++) bfrag[t][k] = make_uint4(0, 0, 0, 0);
+      const float xn = sq + __shfl_xor(sq, 32, 64);
+      const float off = (xn + 2.f * mmax) * (1.f + 0x1p-10f) + 1.f;
+      offs[t] = off;
+      uint32_t o1, o2, o3;
+      split3(0.5f * off, o1, o2, o3);
+      btail[t] = lane < 32 ? make_uint4(BF1 | (BF1 << 16), BF1 | (o1 << 16), o2 | (o3 << 16), 0u)
+                           : make_uint4(0, 0, 0, 0);
     }
-    xn[t] = sq + __shfl_xor(sq, 32, 64);
-  }
 
-  Best best[NTL];
+    uint32_t s1[NTL], s2[NTL];
 #pragma unroll
-  for (int t = 0; t < NTL; t++) best[t] = {-INFINITY, -INFINITY, 0};
-  float mmax = 0.f;
-
-  const uint16_t* C16 = reinterpret_cast<const uint16_t*>(cent) + ((int64_t)u * g.C + cb) * D;
-  for (int c0 = 0; c0 < Cs; c0 += CHUNK) {
-    __syncthreads();
-    // stage centroids c0..c0+CHUNK: 16 lanes per row, 16 bytes each
-    for (int rr = tid >> 4; rr < CHUNK; rr += AT / 16) {
-      const int c = c0 + rr;
-      const int j = tid & 15;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < Cs) v = reinterpret_cast<const uint4*>(C16 + (int64_t)c * D)[j];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[4];
-      float sq = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const float a = __uint_as_float(w[e] << 16), b2 = __uint_as_float(w[e] & 0xFFFF0000u);
-        sq = fmaf(a, a, sq);
-        sq = fmaf(b2, b2, sq);
-        const uint32_t a2 = __float_as_uint(2.f * a) >> 16;
-        const uint32_t bb2 = __float_as_uint(2.f * b2) & 0xFFFF0000u;
-        o[e] = a2 | bb2;
-      }
-      *reinterpret_cast<uint4*>(crow + rr * ROWB + 16 * j) = make_uint4(o[0], o[1], o[2], o[3]);
-      sq += __shfl_xor(sq, 8, 16);
-      sq += __shfl_xor(sq, 4, 16);
-      sq += __shfl_xor(sq, 2, 16);
-      sq += __shfl_xor(sq, 1, 16);
-      if (j == 0) cnorm[rr] = c < Cs ? sq : INFINITY;
-      if (c < Cs) mmax = fmaxf(mmax, sq);
-    }
-    __syncthreads();
-    const int nm = min(CHUNK, Cs - c0);
-    for (int m = 0; m < (nm + 31) / 32; m++) {
-      f32x16_t acc[NTL];
+    for (int t = 0; t < NTL; t++) s1[t] = s2[t] = 0u;
+    // one 32-row tile: 8 k-steps of the dot products and the folded constants
+    auto sweep = [&](int m, f32x16_t* acc) {
 #pragma unroll
       for (int t = 0; t < NTL; t++) acc[t] = (f32x16_t){};
-      const uint8_t* arow = crow + (32 * m + (lane & 31)) * ROWB + 16 * (lane >> 5);
+      const uint8_t* arow = crow + (32 * m + (lane & 31)) * ROWA + 16 * (lane >> 5);
 #pragma unroll
       for (int k = 0; k < 8; k++) {
-        const uint4 av = *reinterpret_cast<const uint4*>(arow + 32 * k);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+        const bf16x8_t a =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow + 32 * k));
 #pragma unroll
         for (int t = 0; t < NTL; t++)
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               a, __builtin_bit_cast(bf16x8_t, bfrag[t][k]), acc[t], 0, 0, 0);
       }
-      // epilogue: lane holds column (lane & 31), rows
-      // 8*(i/4) + 4*(lane>>5) + (i%4) of this 32-row tile
+      // every lane loads (no branch), lanes 32-63 then supply zeros
+      const uint4 tv = ctail[32 * m + (lane & 31)];
+      const bool lo32 = lane < 32;
+      const uint4 av = make_uint4(lo32 ? tv.x : 0u, lo32 ? tv.y : 0u, lo32 ? tv.z : 0u, 0u);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int r0 = 32 * m + 8 * q + 4 * (lane >> 5);
-        const float4 nv = *reinterpret_cast<const float4*>(cnorm + r0);
-        const float nn[4] = {nv.x, nv.y, nv.z, nv.w};
+      for (int t = 0; t < NTL; t++)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, __builtin_bit_cast(bf16x8_t, btail[t]), acc[t], 0, 0, 0);
+    };
+    // epilogue: lane holds column (lane & 31), rows
+    // r = 32 m + 8 (i / 4) + 4 (lane >> 5) + (i % 4); the code 511 - r goes in
+    // the low 9 bits
+    auto fold = [&](int m, const f32x16_t* acc) {
+      const int cm = 511 - 32 * m - 4 * (lane >> 5);
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
+      for (int i = 0; i < 16; i++) {
+        const uint32_t code = (uint32_t)(cm - (8 * (i >> 2) + (i & 3)));
 #pragma unroll
-          for (int t = 0; t < NTL; t++) upd(best[t], acc[t][4 * q + e] - nn[e], c0 + r0 + e);
+        for (int t = 0; t < NTL; t++) {
+          const uint32_t enc = (__float_as_uint(acc[t][i]) & ~511u) | code;
+          s2[t] = max(min(s1[t], s2[t]), min(max(s1[t], s2[t]), enc));  // median (v_med3_u32)
+          s1[t] = max(s1[t], enc);
         }
       }
+    };
+    // two accumulator sets: tile m + 1 is swept while tile m is folded (nm
+    // is even; the last pass sweeps tile nm - 1 again and discards it); then
+    // the next block's points are requested, in flight while the labels are
+    // written
+    f32x16_t accA[NTL], accB[NTL];
+    const int pn = p0 + gridDim.x * BT;
+    sweep(0, accA);
+#pragma unroll 1
+    for (int m = 0; m < nm; m += 2) {
+      sweep(m + 1, accB);
+      fold(m, accA);
+      sweep(min(m + 2, nm - 1), accA);
+      fold(m + 1, accB);
+      // interleave: each MFMA followed by a few epilogue instructions
+#pragma unroll
+      for (int i = 0; i < 36; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
     }
-  }
-  // max |mu|^2 over the segment: reduce over the block
-  mmax = wave_max(mmax);
-  __syncthreads();
-  if (lane == 0) red[wv] = mmax;
-  __syncthreads();
-  mmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (pn < n) load_points(pn, bfrag);
 
 #pragma unroll
-  for (int t = 0; t < NTL; t++) {
-    Best o;
-    o.s1 = __shfl_xor(best[t].s1, 32, 64);
-    o.s2 = __shfl_xor(best[t].s2, 32, 64);
-    o.i1 = __shfl_xor(best[t].i1, 32, 64);
-    const Best bb = merge(best[t], o);
-    const int p = p0 + 64 * wv + 32 * t + (lane & 31);
-    if (lane < 32 && p < n) {
-      const float W = 0x1p-12f * (xn[t] + 2.f * mmax);
-      const int64_t pid = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len + p;
-      if (bb.s2 >= bb.s1 - W) {
-        ws.label[pid] = -1;
-        const int slot = atomicAdd(ws.amb, 1);
-        ws.amb[1 + slot] = (int)pid;
-      } else {
-        ws.label[pid] = bb.i1;
+    for (int t = 0; t < NTL; t++) {
+      const uint32_t o1 = __shfl_xor(s1[t], 32, 64), o2 = __shfl_xor(s2[t], 32, 64);
+      const uint32_t b1 = max(s1[t], o1);
+      const uint32_t b2 = max(min(s1[t], o1), max(s2[t], o2));
+      const int p = p0 + 64 * wv + 32 * t + (lane & 31);
+      if (lane < 32 && p < n) {
+        const float a1 = __uint_as_float(b1 & ~511u), a2 = __uint_as_float(b2 & ~511u);
+        const int64_t pid = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len + p;
+        if (!(a1 - a2 > 0x1p-13f * offs[t])) {
+          ws.label[pid] = -1;
+          const int slot = atomicAdd(ws.amb, 1);
+          ws.amb[1 + slot] = (int)pid;
+        } else {
+          ws.label[pid] = 511 - (int)(b1 & 511u);
+        }
       }
     }
   }
@@ -383,9 +469,13 @@ hipError_t launch_assign(const Geom& g, const void* K, const void* cent, const B
   hipError_t e = launch_zero_i32(ws.amb, 1, s);
   if (e != hipSuccess) return e;
   if (g.dtype == WI_BF16) {
-    const size_t lds = CHUNK * ROWB + CHUNK * 4 + 16;
-    dim3 grid((g.seg_len + 255) / 256, g.U * g.n_seg);
-    WI_LAUNCH(K_ASSIGN, assign_bf16_kernel, grid, dim3(AT), lds, s, g, K, cent, ws);
+    // about one workgroup per CU: each walks several point blocks of its segment
+    const int blocks = (g.seg_len + BT - 1) / BT;
+    const int segs = g.U * g.n_seg;
+    int per = (256 + segs - 1) / segs;
+    if (per > blocks) per = blocks;
+    dim3 grid(per, segs);
+    WI_LAUNCH(K_ASSIGN, assign_bf16_kernel, grid, dim3(BT), BF16_LDS, s, g, K, cent, ws);
   } else {
     const size_t lds = (CHUNK / 2) * ROWF + (CHUNK / 2) * 4 + 16;
     dim3 grid((g.seg_len + 127) / 128, g.U * g.n_seg);
