@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 
 
-def _run(w, k_r, k_e, n_iters=2, batch=None, want_debug=True, scale=0.0, wg=0):
+def _run(w, k_r, k_e, n_iters=2, batch=None, want_debug=True, scale=0.0, wg=0, mutate=None):
     print(f"[decode parity] {w.name} dtype={w.dtype} B={w.batch} H={w.n_kv_heads} "
           f"G={w.group} N={w.n_ctx} seg={w.seg_len} k={w.clusters_per_seg} "
           f"K_r={k_r} K_e={k_e} wg={wg}", flush=True)
@@ -25,6 +25,8 @@ def _run(w, k_r, k_e, n_iters=2, batch=None, want_debug=True, scale=0.0, wg=0):
     od = oracle.make_desc(w.dtype, w.batch, w.n_kv_heads, w.n_ctx, seg_len=w.seg_len,
                           clusters_per_seg=w.clusters_per_seg, n_iters=n_iters)
     idx = oracle.build(od, K, V)
+    if mutate is not None:
+        mutate(idx)
     ns, C, cap, T = oracle.sizes(od)
     gd = wi.make_desc(w.dtype, w.batch, w.n_kv_heads, w.n_ctx, seg_len=w.seg_len,
                       clusters_per_seg=w.clusters_per_seg, n_iters=n_iters)
@@ -152,3 +154,46 @@ def test_decode_multichunk_fp32():
     r = _run(w, 37, 300, wg=1)
     assert r["mism"] == 0
     assert r["err"] <= TOL["f32"]
+
+
+# More clusters per unit than one LDS pass of keys holds (8192): 17 segments
+# of 1024 tokens with 512 clusters each, plus a short one -> C = 8714. The
+# keys are staged in two passes and, with two workgroups per unit, each owns
+# about 4357 clusters (nine chunks).
+LARGE_C = synth.custom(230, "bf16", 1, 8, 2, 68 + 17 * 1024 + 10, 1024, 512, n_needles=4)
+
+
+@pytest.mark.parametrize("wg", [0, 2])
+def test_decode_more_clusters_than_one_key_pass(wg):
+    r = _run(LARGE_C, 300, 2000, n_iters=1, wg=wg)
+    assert r["C"] == 8714
+    assert r["mism"] == 0
+    assert r["err"] <= TOL["bf16"]
+
+
+def _tie_centroids(idx):
+    """Unit 0: every centroid equal (every ranking key ties); unit 1: the first
+    200 centroids equal. Selection then goes by cluster id within the ties,
+    and the pivot's histogram bin holds more keys than one wave ranks."""
+    c = idx["centroids"]
+    c[0, :] = c[0, 0]
+    c[1, :200] = c[1, 0]
+
+
+@pytest.mark.parametrize("k_r,k_e", [(9, 88), (150, 40)])
+def test_decode_tied_keys(k_r, k_e):
+    r = _run(SMALL, k_r, k_e, mutate=_tie_centroids)
+    assert r["mism"] == 0
+    assert r["err"] <= TOL["bf16"]
+    sel = r["sel"]
+    assert sel[0].tolist() == list(range(k_r + min(k_e, r["C"] - k_r)))
+
+
+def test_decode_tied_keys_more_clusters_than_one_key_pass():
+    def tie(idx):
+        c = idx["centroids"]
+        c[0, :] = c[0, 0]
+    r = _run(LARGE_C, 300, 2000, n_iters=1, mutate=tie)
+    assert r["mism"] == 0
+    assert r["err"] <= TOL["bf16"]
+    assert r["sel"][0].tolist() == list(range(2300))
