@@ -72,12 +72,15 @@ def exec_reference(idx: dict, sel: np.ndarray, k_r: int, n_ctx: int, T: int, n_s
     return res
 
 
-def index_to_host(ix: wi.Index) -> dict:
-    return dict(centroids=to_np(ix.centroids), sizes=to_np(ix.cluster_size),
-                vsum=to_np(ix.value_sum), block_off=to_np(ix.block_off), kblk=to_np(ix.k_blocks),
-                vblk=to_np(ix.v_blocks), slot_token=to_np(ix.slot_token),
-                steady_k=to_np(ix.steady_k), steady_v=to_np(ix.steady_v),
-                assign=to_np(ix.assign))
+def index_to_host(ix: wi.Index, units=None) -> dict:
+    """Index arrays on the host, [U, ...]; with units, only those units (in
+    the order given)."""
+    pick = (lambda t: t) if units is None else (lambda t: t[list(units)])  # noqa: E731
+    return dict(centroids=to_np(pick(ix.centroids)), sizes=to_np(pick(ix.cluster_size)),
+                vsum=to_np(pick(ix.value_sum)), block_off=to_np(pick(ix.block_off)),
+                kblk=to_np(pick(ix.k_blocks)), vblk=to_np(pick(ix.v_blocks)),
+                slot_token=to_np(pick(ix.slot_token)), steady_k=to_np(pick(ix.steady_k)),
+                steady_v=to_np(pick(ix.steady_v)), assign=to_np(pick(ix.assign)))
 
 
 def assert_index_equal(got: dict, ref: dict, units=None, n_st=68):

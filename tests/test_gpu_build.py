@@ -99,15 +99,13 @@ def test_build_deterministic():
     assert_index_equal(a, b)
 
 
-@pytest.mark.slow
-def test_build_and_decode_llama8b_128k_sampled_units():
-    """The 128K Llama3.1-8B-shaped layer at full size, in the benchmark's launch
-    configuration (all 8 KV heads in one call). The oracle rebuilds two sampled
-    units from the same seeded inputs; their index must match bit-for-bit and
-    their decode outputs within the bf16 tolerance."""
+def _full_size_sampled(w, units):
+    """Build and decode a whole workload in one call each (the benchmark's
+    launch configuration); the oracle rebuilds the sampled units from the
+    same seeded inputs, whose index must match bit-for-bit and whose decode
+    outputs must be within the bf16 tolerance."""
     from parity import rel_err, upload_q
-    w = synth.WORKLOADS[1]
-    print(f"[full-size parity] {w.name}", flush=True)
+    print(f"[full-size parity] {w.name} units {units}", flush=True)
     K, V, q = synth.gen_batch(w)
     gd, _ = descs(w)
     kt, vt = upload_kv(K, V, w.dtype)
@@ -117,16 +115,40 @@ def test_build_and_decode_llama8b_128k_sampled_units():
     out = wi.decode_attention(ix, dd, upload_q(q, w.dtype))
     torch.cuda.synchronize()
     out = out.cpu().numpy()
-    got = index_to_host(ix)
-    del kt, vt
-    od = oracle.make_desc("bf16", 1, w.n_kv_heads, w.n_ctx, n_iters=w.n_iters)
-    units = (0, 5)
-    ref = oracle.build(od, K, V, units=units)
-    assert_index_equal(got, ref, units=units)
-    for h in units:
-        sub = {k: v[h:h + 1] for k, v in ref.items()}
-        od1 = oracle.make_desc("bf16", 1, 1, w.n_ctx, n_iters=w.n_iters)
-        r = oracle.decode(od1, w.group, k_r, k_e, sub, q[:, h * w.group:(h + 1) * w.group])
-        e = rel_err(out[:, h * w.group:(h + 1) * w.group], r["out"])
-        print(f"  unit h={h}: index exact, decode rel err {e:.3e}", flush=True)
+    got = index_to_host(ix, units)  # the sampled units only, in order
+    del kt, vt, ix
+    H = w.n_kv_heads
+    # the oracle builds only the sampled units, over the leading sequences
+    # that hold them (so each keeps its (sequence, head) random stream)
+    bmax = max(units) // H + 1
+    od = oracle.make_desc("bf16", bmax, H, w.n_ctx, n_iters=w.n_iters)
+    ref = oracle.build(od, K[:bmax], V[:bmax], units=units)
+    ref = {k: v[list(units)] for k, v in ref.items()}
+    assert_index_equal(got, ref)
+    od1 = oracle.make_desc("bf16", 1, 1, w.n_ctx, n_iters=w.n_iters)
+    for i, u in enumerate(units):
+        b, h = divmod(u, H)
+        sub = {k: v[i:i + 1] for k, v in ref.items()}
+        qu = q[b:b + 1, h * w.group:(h + 1) * w.group]
+        r = oracle.decode(od1, w.group, k_r, k_e, sub, qu)
+        e = rel_err(out[b:b + 1, h * w.group:(h + 1) * w.group], r["out"])
+        print(f"  unit (b={b}, h={h}): index exact, decode rel err {e:.3e}", flush=True)
         assert e <= 2e-3
+
+
+@pytest.mark.slow
+def test_build_and_decode_llama8b_128k_sampled_units():
+    _full_size_sampled(synth.WORKLOADS[1], (0, 5))
+
+
+@pytest.mark.slow
+def test_build_and_decode_llama8b_128k_batch8_sampled_units():
+    """64 units in one call (4 select/attend workgroups per unit)."""
+    _full_size_sampled(synth.WORKLOADS[2], (2, 14))
+
+
+@pytest.mark.slow
+def test_build_and_decode_qwen7b_256k_batch4_sampled_units():
+    """16 384 clusters per unit (two LDS passes of keys), 7 query heads per KV
+    head, anisotropic keys."""
+    _full_size_sampled(synth.WORKLOADS[3], (2, 5))
