@@ -169,6 +169,23 @@ def main():
     wall = time.perf_counter() - t_start
     step_ms = ev0.elapsed_time(ev1) / a.steps
 
+    # the same steps replayed from a HIP graph (one decode call per index copy,
+    # captured once): launch overhead between the two kernels of a step
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for j in range(len(copies)):
+            wi.decode_attention(copies[j], dd, qt, out=outs[j], ws=wsd)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, a.steps // len(copies))
+    ev0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    graph_step_ms = ev0.elapsed_time(ev1) / (reps * len(copies))
+    del graph
+
     # per-kernel durations over the same number of steps (timing hook)
     wi.timing_start()
     for i in range(a.steps):
@@ -213,6 +230,8 @@ def main():
                    "seg_len": w.seg_len, "clusters_per_seg": w.clusters_per_seg,
                    "k_retrieve": k_r, "k_estimate": k_e_eff, "index_copies": len(copies)},
         "step_hbm_GBps": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+        "graph_replay": {"ms_per_step": round(graph_step_ms, 5),
+                         "queries_per_s": round(w.batch / (graph_step_ms * 1e-3), 1)},
         "step_bytes": int(step_bytes),
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,

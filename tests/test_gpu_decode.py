@@ -197,3 +197,28 @@ def test_decode_tied_keys_more_clusters_than_one_key_pass():
     assert r["mism"] == 0
     assert r["err"] <= TOL["bf16"]
     assert r["sel"][0].tolist() == list(range(2300))
+
+
+def test_decode_graph_replay_matches_eager():
+    """A decode call captured in a HIP graph and replayed several times, with
+    eager decode calls of another query between the replays, gives the eager
+    output bit for bit on every replay."""
+    r = _run(SMALL, 9, 88, want_debug=False)
+    gix, dd, qt = r["gix"], r["dd"], r["qt"]
+    q2 = torch.flip(qt, dims=[1]).contiguous()
+    eager = wi.decode_attention(gix, dd, qt)
+    torch.cuda.synchronize()
+    ref = eager.cpu().numpy().view(np.uint32).copy()
+    out = torch.empty_like(eager)
+    ws = torch.empty(wi.decode_sizes(gix.desc, dd), dtype=torch.uint8, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wi.decode_attention(gix, dd, qt, out=out, ws=ws)
+    for _ in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref)
+        other = wi.decode_attention(gix, dd, q2, ws=ws)  # eager work on the same workspace
+        torch.cuda.synchronize()
+        assert not np.array_equal(other.cpu().numpy().view(np.uint32), ref)
