@@ -75,6 +75,61 @@ __device__ __forceinline__ float dist32(const void* row, const float* mu) {
   return acc;
 }
 
+// The same sum, stopped early once it cannot end below `bound`. Every term
+// is a square, and a round-to-nearest fused multiply-add of a non-negative
+// product onto acc never lowers acc, so the running value only grows: once
+// it is >= bound (or NaN, or bound is NaN) the full sum is not below bound
+// either, and the caller's `dist < bound` test comes out false both ways.
+// The row is read in 32-dimension chunks, so a point the new centroid cannot
+// claim usually costs one chunk of its row instead of all of it. Returns the
+// full sum whenever that sum is below bound.
+// The first chunk is loaded by the caller (early, before the pick is
+// known) and passed in; the rest is read only while the sum stays below bound.
+template <int DT>
+struct Chunk {
+  uint4 v[DT == WI_BF16 ? 4 : 8];  // 32 dimensions
+};
+
+template <int DT>
+__device__ __forceinline__ Chunk<DT> load_chunk(const void* row, int ch) {
+  constexpr int VPC = DT == WI_BF16 ? 4 : 8;
+  Chunk<DT> c;
+#pragma unroll
+  for (int j = 0; j < VPC; j++) c.v[j] = reinterpret_cast<const uint4*>(row)[VPC * ch + j];
+  return c;
+}
+
+template <int DT>
+__device__ __forceinline__ float add_chunk(float acc, const Chunk<DT>& c, const float* m) {
+  constexpr int VPC = DT == WI_BF16 ? 4 : 8;
+#pragma unroll
+  for (int j = 0; j < VPC; j++) {
+    const uint32_t w[4] = {c.v[j].x, c.v[j].y, c.v[j].z, c.v[j].w};
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      if constexpr (DT == WI_BF16) {
+        const float e0 = __uint_as_float(w[t] << 16) - m[8 * j + 2 * t];
+        acc = __builtin_fmaf(e0, e0, acc);
+        const float e1 = __uint_as_float(w[t] & 0xFFFF0000u) - m[8 * j + 2 * t + 1];
+        acc = __builtin_fmaf(e1, e1, acc);
+      } else {
+        const float e0 = __uint_as_float(w[t]) - m[4 * j + t];
+        acc = __builtin_fmaf(e0, e0, acc);
+      }
+    }
+  }
+  return acc;
+}
+
+template <int DT>
+__device__ __forceinline__ float dist32_below(const void* row, const Chunk<DT>& c0,
+                                             const float* mu, float bound) {
+  float acc = add_chunk<DT>(0.f, c0, mu);
+#pragma unroll 1
+  for (int ch = 1; ch < 4 && acc < bound; ch++) acc = add_chunk<DT>(acc, load_chunk<DT>(row, ch), mu + 32 * ch);
+  return acc;
+}
+
 template <int DT>
 __device__ __forceinline__ void load_mu(const void* row, float* mu) {
   const int t = threadIdx.x;
@@ -207,8 +262,11 @@ __global__ __launch_bounds__(NT) void kpp_weights_kernel(Geom g, BuildWs ws, int
 }
 
 // Round r >= 1: derive pick r from round r-1, update distances and weights.
+// What does not depend on the pick (the point's distance, the first chunk of
+// its row, the segment's slice partials) is requested first, so those reads
+// overlap the pick's derivation.
 template <int DT>
-__global__ __launch_bounds__(NT) void kpp_round_kernel(Geom g, const void* __restrict__ K,
+__global__ __launch_bounds__(NT, DT == WI_BF16 ? 8 : 5) void kpp_round_kernel(Geom g, const void* __restrict__ K,
                                                         void* __restrict__ cent, BuildWs ws,
                                                         int nsl, int r) {
   const int gs = blockIdx.y, slice = blockIdx.x;
@@ -230,14 +288,24 @@ __global__ __launch_bounds__(NT) void kpp_round_kernel(Geom g, const void* __res
   __shared__ unsigned long long tq_s;
   __shared__ int q_s;
   const KppPartial* kp = ws.kpp + (int64_t)gs * nsl;
+  const int64_t first = seg_first(g, s);
 
-  float mx = tid < ns ? kp[tid].maxd : 0.f;
-  mx = block_max_f32(mx, redf);
+  // pick-independent reads first
+  const int i = slice * NT + tid;
+  const bool in = i < n;
+  const int64_t pid = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len + i;
+  const void* row = krow<DT>(K, g, u, first + (in ? i : 0));
+  const float dcur = in ? ws.D[pid] : 0.f;
+  const Chunk<DT> c0 = load_chunk<DT>(row, 0);
+  const float mxl = tid < ns ? kp[tid].maxd : 0.f;
+  const unsigned long long v = (wv == 0 && lane < ns) ? kp[lane].sum[pin] : 0ull;
+  int mun = (wv == 0 && lane < ns) ? kp[lane].minun[pin] : 0x7FFFFFFF;
+
+  const float mx = block_max_f32(mxl, redf);
   const int F = mx > 0.f ? weight_shift(mx, n) : 0;
 
   // total weight and owner slice (wave 0; ns <= 32 slices)
   if (wv == 0) {
-    const unsigned long long v = lane < ns ? kp[lane].sum[pin] : 0ull;
     unsigned long long incl = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -245,7 +313,6 @@ __global__ __launch_bounds__(NT) void kpp_round_kernel(Geom g, const void* __res
       if (lane >= o) incl += y;
     }
     const unsigned long long W = __shfl(incl, 63, 64);
-    int mun = lane < ns ? kp[lane].minun[pin] : 0x7FFFFFFF;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mun = min(mun, __shfl_xor(mun, o, 64));
     if (W == 0ull) {
@@ -269,8 +336,8 @@ __global__ __launch_bounds__(NT) void kpp_round_kernel(Geom g, const void* __res
     const unsigned long long tq = tq_s;
     const int nq = min(NT, n - q * NT);
     const int64_t qbase = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len + (int64_t)q * NT;
-    const unsigned long long v = tid < nq ? ws.w[pin][qbase + tid] : 0ull;
-    unsigned long long incl = v;
+    const unsigned long long wq = tid < nq ? ws.w[pin][qbase + tid] : 0ull;
+    unsigned long long incl = wq;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const unsigned long long y = __shfl_up(incl, o, 64);
@@ -281,23 +348,21 @@ __global__ __launch_bounds__(NT) void kpp_round_kernel(Geom g, const void* __res
     unsigned long long off = 0;
     for (int w2 = 0; w2 < wv; w2++) off += wscan[w2];
     incl += off;
-    if (tid < nq && incl > tq && incl - v <= tq) pick_s = q * NT + tid;
+    if (tid < nq && incl > tq && incl - wq <= tq) pick_s = q * NT + tid;
   }
   __syncthreads();
   const int pick = pick_s;
-  const int64_t first = seg_first(g, s);
   const void* rp = krow<DT>(K, g, u, first + pick);
   load_mu<DT>(rp, mu);
   if (slice == 0) store_centroid<DT>(cent, (int64_t)u * g.C + seg_cbase(g, s) + r, rp);
   __syncthreads();
 
-  const int i = slice * NT + tid;
-  const int64_t pid = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len + i;
   unsigned long long w = 0;
   int un = 0x7FFFFFFF;
-  if (i < n) {
-    float d = ws.D[pid];
-    const float dn = dist32<DT>(krow<DT>(K, g, u, first + i), mu);
+  if (in) {
+    float d = dcur;
+    // a point at distance 0 cannot get closer; skip its row
+    const float dn = d > 0.f ? dist32_below<DT>(row, c0, mu, d) : d;
     if (dn < d) {
       d = dn;
       ws.D[pid] = d;
@@ -312,10 +377,10 @@ __global__ __launch_bounds__(NT) void kpp_round_kernel(Geom g, const void* __res
     if (!ch) un = i;
   }
   const unsigned long long tot = block_sum_u64(w, red64);
-  const int mun = block_min_i32(un, redi);
+  const int mn = block_min_i32(un, redi);
   if (tid == 0) {
     ws.kpp[(int64_t)gs * nsl + slice].sum[pout] = tot;
-    ws.kpp[(int64_t)gs * nsl + slice].minun[pout] = mun;
+    ws.kpp[(int64_t)gs * nsl + slice].minun[pout] = mn;
   }
 }
 
