@@ -137,6 +137,8 @@ wi_status wi_index_sizes(const wi_index_desc *desc, int64_t *n_segments,
  *   the last assignment's membership and the last update's centroids.
  *   ws            device workspace of >= workspace_bytes from
  *                 wi_index_sizes; contents on entry are ignored.
+ *   bufs->k_blocks also serves as scratch during k-means++ seeding, before
+ *   its final contents are written; no output may overlap k or v.
  */
 wi_status wi_build_index(const wi_index_desc *desc, const void *k,
                          const void *v, const void *init_centroids,

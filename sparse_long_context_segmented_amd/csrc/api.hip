@@ -314,6 +314,10 @@ wi_status wi_build_index(const wi_index_desc* desc, const void* k, const void* v
   wi::BuildWs w;
   carve_build(g, reinterpret_cast<uint8_t*>(ws), &w);
 
+  // k_blocks holds >= U * n_idx key rows (block_cap * T >= n_idx) and is
+  // written only by the layout step, so k-means++ keeps its chunked copy of
+  // the keys there until then
+  w.kc = bufs->k_blocks;
   if (init_centroids)
     CHECK_HIP(wi::launch_copy_init(g, init_centroids, bufs->centroids, stream), "copy init");
   else

@@ -90,12 +90,14 @@ struct Chunk {
   uint4 v[DT == WI_BF16 ? 4 : 8];  // 32 dimensions
 };
 
+// Chunk ch of a point from the chunk-major key copy: `base` is the point's
+// first chunk, chunks of one point lie `cstride` 16-byte vectors apart.
 template <int DT>
-__device__ __forceinline__ Chunk<DT> load_chunk(const void* row, int ch) {
+__device__ __forceinline__ Chunk<DT> load_chunk(const uint4* base, int64_t cstride, int ch) {
   constexpr int VPC = DT == WI_BF16 ? 4 : 8;
   Chunk<DT> c;
 #pragma unroll
-  for (int j = 0; j < VPC; j++) c.v[j] = reinterpret_cast<const uint4*>(row)[VPC * ch + j];
+  for (int j = 0; j < VPC; j++) c.v[j] = base[ch * cstride + j];
   return c;
 }
 
@@ -122,11 +124,12 @@ __device__ __forceinline__ float add_chunk(float acc, const Chunk<DT>& c, const 
 }
 
 template <int DT>
-__device__ __forceinline__ float dist32_below(const void* row, const Chunk<DT>& c0,
-                                             const float* mu, float bound) {
+__device__ __forceinline__ float dist32_below(const uint4* base, int64_t cstride,
+                                             const Chunk<DT>& c0, const float* mu, float bound) {
   float acc = add_chunk<DT>(0.f, c0, mu);
 #pragma unroll 1
-  for (int ch = 1; ch < 4 && acc < bound; ch++) acc = add_chunk<DT>(acc, load_chunk<DT>(row, ch), mu + 32 * ch);
+  for (int ch = 1; ch < 4 && acc < bound; ch++)
+    acc = add_chunk<DT>(acc, load_chunk<DT>(base, cstride, ch), mu + 32 * ch);
   return acc;
 }
 
@@ -222,7 +225,15 @@ __global__ __launch_bounds__(NT) void kpp_init_kernel(Geom g, const void* __rest
   const int64_t pid = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len + i;
   float d = 0.f;
   if (i < n) {
-    d = dist32<DT>(krow<DT>(K, g, u, first + i), mu);
+    // the chunk-major copy the rounds read: chunk c of point pid at vectors
+    // (c * U n_idx + pid) * VPC ..
+    constexpr int VPC = DT == WI_BF16 ? 4 : 8;
+    const uint4* row = reinterpret_cast<const uint4*>(krow<DT>(K, g, u, first + i));
+    uint4* kc = reinterpret_cast<uint4*>(ws.kc);
+    const int64_t cstride = (int64_t)g.U * g.n_idx * VPC;
+#pragma unroll
+    for (int j = 0; j < 4 * VPC; j++) kc[(j / VPC) * cstride + pid * VPC + (j % VPC)] = row[j];
+    d = dist32<DT>(row, mu);
     ws.D[pid] = d;
     ws.chosen[pid] = (i == i0);
   }
@@ -294,9 +305,11 @@ __global__ __launch_bounds__(NT, DT == WI_BF16 ? 8 : 5) void kpp_round_kernel(Ge
   const int i = slice * NT + tid;
   const bool in = i < n;
   const int64_t pid = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len + i;
-  const void* row = krow<DT>(K, g, u, first + (in ? i : 0));
+  constexpr int VPC = DT == WI_BF16 ? 4 : 8;
+  const int64_t cstride = (int64_t)g.U * g.n_idx * VPC;
+  const uint4* kc = reinterpret_cast<const uint4*>(ws.kc) + (in ? pid : 0) * VPC;
   const float dcur = in ? ws.D[pid] : 0.f;
-  const Chunk<DT> c0 = load_chunk<DT>(row, 0);
+  const Chunk<DT> c0 = load_chunk<DT>(kc, cstride, 0);
   const float mxl = tid < ns ? kp[tid].maxd : 0.f;
   const unsigned long long v = (wv == 0 && lane < ns) ? kp[lane].sum[pin] : 0ull;
   int mun = (wv == 0 && lane < ns) ? kp[lane].minun[pin] : 0x7FFFFFFF;
@@ -362,7 +375,7 @@ __global__ __launch_bounds__(NT, DT == WI_BF16 ? 8 : 5) void kpp_round_kernel(Ge
   if (in) {
     float d = dcur;
     // a point at distance 0 cannot get closer; skip its row
-    const float dn = d > 0.f ? dist32_below<DT>(row, c0, mu, d) : d;
+    const float dn = d > 0.f ? dist32_below<DT>(kc, cstride, c0, mu, d) : d;
     if (dn < d) {
       d = dn;
       ws.D[pid] = d;

@@ -72,6 +72,10 @@ struct BuildWs {
   int* seg_blocks;             // [U*n_seg] blocks used by each segment
   int* seg_bbase;              // [U*n_seg] first block of each segment
   int* unit_used;              // [U] blocks used by each unit
+  void* kc;                    // [4][U*n_idx][32] dtype: the indexed keys in
+                               // 32-dimension chunks, chunk-major (k-means++
+                               // only; lives in the k_blocks output, which the
+                               // layout step writes afterwards)
 };
 constexpr int KPP_SLICE = 256;  // points per k-means++ workgroup
 
