@@ -98,8 +98,11 @@ __device__ __forceinline__ void split3(float x, uint32_t& h1, uint32_t& h2, uint
 }
 
 // Workgroup (blockIdx.x, segment) handles the segment's 512-point blocks
-// blockIdx.x, blockIdx.x + gridDim.x, ...: the centroids are staged once, and
-// the next block's points are loaded during the current block's MFMA sweep.
+// blockIdx.x, blockIdx.x + gridDim.x, ...: the centroids are staged once.
+// Its waves take 64-point units of those blocks from a counter in LDS
+// (unit j = block j / 8, 64-point column j % 8), so a wave that the issue
+// order favours does more units and all waves end together; the next unit's
+// points are requested while the current unit's labels are written.
 __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* __restrict__ K,
                                                             const void* __restrict__ cent,
                                                             BuildWs ws) {
@@ -120,10 +123,10 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
 
   // B fragments of a block: point p = p0 + 64 wv + 32 t + (lane & 31), dims
   // 16 k + 8 (lane >> 5) .. + 8, for k = 0..7
-  auto load_points = [&](int p0, uint4 (*bf)[8]) {
+  auto load_points = [&](int pb, uint4 (*bf)[8]) {
 #pragma unroll
     for (int t = 0; t < NTL; t++) {
-      const int p = min(p0 + 64 * wv + 32 * t + (lane & 31), n - 1);  // clamped; not written
+      const int p = min(pb + 32 * t + (lane & 31), n - 1);  // clamped; not written
       const uint4* row = reinterpret_cast<const uint4*>(kptr<WI_BF16>(K, g, u, first + p));
 #pragma unroll
       for (int k = 0; k < 8; k++) bf[t][k] = row[2 * k + (lane >> 5)];
@@ -131,7 +134,10 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
   };
   // the first block's points are requested before the centroids
   uint4 bfrag[NTL][8];
-  load_points(blockIdx.x * BT, bfrag);
+  __shared__ int next_unit;
+  auto unit_base = [&](int j) { return ((int)blockIdx.x + (j >> 3) * (int)gridDim.x) * BT + 64 * (j & 7); };
+  int pb = unit_base(wv);  // units 0..7 go to waves 0..7
+  load_points(pb, bfrag);
   // stage the segment's centroids: 16 lanes per row, 16 bytes each, 32 rows
   // per pass; |mu|^2 per row in float32 (fixed order), A tails from it
   const uint16_t* C16 = reinterpret_cast<const uint16_t*>(cent) + ((int64_t)u * g.C + cb) * D;
@@ -172,6 +178,7 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
       }
     }
   }
+  if (tid == 0) next_unit = BT / 64;
   mmax = wave_max(mmax);
   if (lane == 0) red[wv] = mmax;
   __syncthreads();
@@ -180,7 +187,7 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
   const int nm = Cp / 32;
 
 #pragma unroll 1
-  for (int p0 = blockIdx.x * BT; p0 < n; p0 += gridDim.x * BT) {
+  while (pb < n) {
 
     // per point: |x|^2, the offset and the B tail [1, 1, 1, o1, o2, o3, 0, 0]
     // (lanes 0-31 supply k = 0..7 of the extra step; lanes 32-63 zeros)
@@ -240,14 +247,19 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
     // the low 9 bits
     auto fold = [&](int m, const f32x16_t* acc) {
       const int cm = 511 - 32 * m - 4 * (lane >> 5);
+      // two scores at a time: the best of {s1, e0, e1} is a three-input max,
+      // the second best of {s1, s2, e0, e1} the larger of s2 and the median
+      // of {s1, e0, e1} (s1 >= s2 holds throughout)
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const uint32_t code = (uint32_t)(cm - (8 * (i >> 2) + (i & 3)));
+      for (int i = 0; i < 16; i += 2) {
+        const uint32_t code = (uint32_t)(cm - (8 * (i >> 2) + (i & 3)));  // row i + 1: code - 1
 #pragma unroll
         for (int t = 0; t < NTL; t++) {
-          const uint32_t enc = (__float_as_uint(acc[t][i]) & ~511u) | code;
-          s2[t] = max(min(s1[t], s2[t]), min(max(s1[t], s2[t]), enc));  // median (v_med3_u32)
-          s1[t] = max(s1[t], enc);
+          const uint32_t e0 = (__float_as_uint(acc[t][i]) & ~511u) | code;
+          const uint32_t e1 = (__float_as_uint(acc[t][i + 1]) & ~511u) | (code - 1u);
+          const uint32_t md = max(min(e0, e1), min(max(e0, e1), s1[t]));  // v_med3_u32
+          s1[t] = max(max(s1[t], e0), e1);                                // v_max3_u32
+          s2[t] = max(s2[t], md);
         }
       }
     };
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
     // the next block's points are requested, in flight while the labels are
     // written
     f32x16_t accA[NTL], accB[NTL];
-    const int pn = p0 + gridDim.x * BT;
+
     sweep(0, accA);
 #pragma unroll 1
     for (int m = 0; m < nm; m += 2) {
@@ -271,6 +283,9 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
     }
+    int jn = 0;
+    if (lane == 0) jn = atomicAdd(&next_unit, 1);
+    const int pn = unit_base(__builtin_amdgcn_readfirstlane(jn));
     if (pn < n) load_points(pn, bfrag);
 
 #pragma unroll
@@ -278,7 +293,7 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
       const uint32_t o1 = __shfl_xor(s1[t], 32, 64), o2 = __shfl_xor(s2[t], 32, 64);
       const uint32_t b1 = max(s1[t], o1);
       const uint32_t b2 = max(min(s1[t], o1), max(s2[t], o2));
-      const int p = p0 + 64 * wv + 32 * t + (lane & 31);
+      const int p = pb + 32 * t + (lane & 31);
       if (lane < 32 && p < n) {
         const float a1 = __uint_as_float(b1 & ~511u), a2 = __uint_as_float(b2 & ~511u);
         const int64_t pid = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len + p;
@@ -291,6 +306,7 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
         }
       }
     }
+    pb = pn;
   }
 }
 
