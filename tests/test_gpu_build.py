@@ -83,6 +83,29 @@ def test_build_singleton_clusters_and_short_segments():
     assert np.all(got["sizes"] == 1)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_build_duplicate_keys(dtype):
+    """Every indexed key is one of five rows: after five picks every distance
+    is 0, so k-means++ sees zero total weight and takes the smallest unchosen
+    index (and never reads a row whose distance is already 0); Lloyd then
+    has exact distance ties between duplicate centroids (lowest id wins) and
+    many empty clusters."""
+    w = synth.custom(303 if dtype == "bf16" else 304, dtype, 1, 4, 2, 68 + 2 * 1024 + 100,
+                     1024, 64, n_iters=3, n_needles=2)
+    print(f"[build parity] duplicate keys dtype={dtype}", flush=True)
+    K, V, q = synth.gen_batch(w)
+    pick = np.random.default_rng(11).integers(0, 5, size=(w.n_kv_heads, w.n_ctx - 68))
+    for h in range(w.n_kv_heads):
+        K[0, h, 4:w.n_ctx - 64] = K[0, h, 4:9][pick[h]]
+    gd, od = descs(w)
+    ref = oracle.build(od, K, V)
+    kt, vt = upload_kv(K, V, w.dtype)
+    got = index_to_host(wi.build_index(gd, kt, vt))
+    torch.cuda.synchronize()
+    assert_index_equal(got, ref)
+    assert (ref["sizes"] == 0).sum() > 0
+
+
 def test_build_strided_kv_and_layer_seed():
     got, ref, _ = _build_both(SMALL, layer=7, strided=True)
     assert_index_equal(got, ref)
