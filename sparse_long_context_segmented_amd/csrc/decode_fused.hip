@@ -23,8 +23,10 @@
 //     2048-bin histogram linear in key value over the unit's key range (the
 //     score step publishes each of its workgroups' minimum and maximum), built
 //     as the keys arrive, locates the pivot's bin; its keys (at most
-//     CAND_MAX) are ranked exactly by one wave, a fuller bin falls back to an
-//     8-pass radix select over comp within that bin. The
+//     CAND_MAX) are ranked exactly by four waves, one key per lane (the bin
+//     at the estimation pivot of a 1M-token unit holds about 130 of its 65536
+//     keys); a fuller bin falls back to an 8-pass radix select over comp
+//     within that bin. The
 //     sizes, block offsets and estimation logits of the workgroup's first
 //     512 own clusters are loaded at kernel start, behind the selection.
 //  2. Own clusters, 512 at a time: one block scan gives each retrieved
@@ -64,12 +66,13 @@ constexpr int CL = 8192;           // keys staged in LDS at a time
 constexpr int KPT = CL / NT;       // staged keys per thread
 constexpr int NBINS = 2048;
 constexpr int BPT = NBINS / NT;    // histogram bins per thread
-constexpr int CAND_MAX = 64;       // pivot-bin keys ranked by one wave
+constexpr int CAND_MAX = 256;      // pivot-bin keys ranked on chip (4 waves per pivot)
 constexpr int GRP = 16;            // consecutive cluster ids per ownership group
 constexpr int EB = 16;             // estimation clusters per wave block
 constexpr int PI_MAX = 32 + EB;    // items per wave block (tokens + clusters)
 constexpr int PART = 2 + D;        // m, l, acc[128]
 static_assert(NT == 512 && BPT == 4 && KPT % 4 == 0, "thread layout");
+static_assert(CAND_MAX <= 4 * 64 && NW == 8, "four waves rank each pivot's candidates");
 
 struct FusedArgs {
   const uint32_t* key;     // [U][Cp] order-preserving ranking keys
@@ -462,23 +465,35 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // ---- 1e. pivots: wave t ranks the keys of target t's bin -------------------
+  // ---- 1e. pivots: waves 4t .. 4t + 3 rank the keys of target t's bin, one
+  // candidate per lane (candidate 64 (wv % 4) + lane); up to 64 candidates
+  // one wave compares through lane reads, more through LDS reads --------------
   const int nc0 = ncand[0], nc1 = ncand[1];
-  if (wv < 2) {
-    const int t = wv;
+  {
+    const int t = wv >> 2, qw = wv & 3;
     const bool need = t == 0 ? need0 : need1;
     const int nc = t == 0 ? nc0 : nc1;
-    if (need && nc <= CAND_MAX) {
-      const uint32_t kk = lane < nc ? candk[t * CAND_MAX + lane] : 0u;
-      const int id = lane < nc ? candi[t * CAND_MAX + lane] : INT_MAX;
+    if (need && nc <= CAND_MAX && 64 * qw < nc) {
+      const int i = 64 * qw + lane;
+      const uint32_t kk = i < nc ? candk[t * CAND_MAX + i] : 0u;
+      const int id = i < nc ? candi[t * CAND_MAX + i] : INT_MAX;
       int rank = 0;
+      if (nc <= 64) {
 #pragma unroll 1
-      for (int j = 0; j < nc; j++) {
-        const uint32_t kj = (uint32_t)rdl((int)kk, j);
-        const int idj = rdl(id, j);
-        rank += (kj > kk) || (kj == kk && idj < id);
+        for (int j = 0; j < nc; j++) {
+          const uint32_t kj = (uint32_t)rdl((int)kk, j);
+          const int idj = rdl(id, j);
+          rank += (kj > kk) || (kj == kk && idj < id);
+        }
+      } else {
+#pragma unroll 1
+        for (int j = 0; j < nc; j++) {
+          const uint32_t kj = candk[t * CAND_MAX + j];
+          const int idj = candi[t * CAND_MAX + j];
+          rank += (kj > kk) || (kj == kk && idj < id);
+        }
       }
-      if (lane < nc && rank == bneed[t] - 1) {
+      if (i < nc && rank == bneed[t] - 1) {
         pk[t] = kk;
         pi[t] = id;
       }

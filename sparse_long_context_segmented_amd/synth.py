@@ -175,3 +175,49 @@ def gen_batch(w: Workload, layer: int = 0, heads=None, batches=None):
         vs.append(np.stack(vb))
         qs.append(np.concatenate(qb, axis=0))
     return np.stack(ks), np.stack(vs), np.stack(qs)
+
+
+def gen_layer_device(w: Workload, layer: int, device, heads_per_draw: int = 2):
+    """Draw one layer of a workload on the GPU with torch's own generator.
+
+    Same recipe as gen_unit (mixture keys, needles, optional anisotropic
+    scales, N(0, 1) values, needle-biased queries), but the draws come from a
+    torch CUDA generator seeded with (workload, layer), not from numpy's
+    per-unit streams, so the values differ from gen_batch. Used only to time
+    workloads whose raw KV is too large to draw on the host (the 32-layer
+    1M-token model, 4.3 GB of raw KV per layer); parity at that size is
+    checked on host-drawn units. Returns K, V [B, Hkv, N, 128] and
+    q [B, Hq, 128] in the workload dtype.
+    """
+    import torch
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed((w.wid << 20) ^ (layer + 1))
+    B, H, N, d = w.batch, w.n_kv_heads, w.n_ctx, HEAD_DIM
+    K = torch.empty(B, H, N, d, dtype=dt, device=device)
+    V = torch.empty(B, H, N, d, dtype=dt, device=device)
+    q = torch.empty(B, w.n_q_heads, d, dtype=dt, device=device)
+    lo, hi = N_SINK, N - N_LOCAL
+    n_needles = min(w.n_needles, max(hi - lo, 0))
+    for b in range(B):
+        for h0 in range(0, H, heads_per_draw):
+            h1 = min(H, h0 + heads_per_draw)
+            nh = h1 - h0
+            means = torch.randn(nh, w.n_components, d, generator=gen, device=device)
+            labels = torch.randint(0, w.n_components, (nh, N), generator=gen, device=device)
+            k = torch.gather(means, 1, labels[..., None].expand(nh, N, d))
+            k += 0.3 * torch.randn(nh, N, d, generator=gen, device=device)
+            needle = torch.randn(nh, d, generator=gen, device=device)
+            for j in range(nh):
+                pos = torch.randperm(hi - lo, generator=gen, device=device)[:n_needles] + lo
+                k[j, pos] = needle[j][None, :] + 0.3 * torch.randn(
+                    n_needles, d, generator=gen, device=device)
+            if w.anisotropic:
+                k *= torch.exp(0.5 * torch.randn(nh, 1, d, generator=gen, device=device))
+            K[b, h0:h1] = k.to(dt)
+            del k, labels, means
+            V[b, h0:h1] = torch.randn(nh, N, d, generator=gen, device=device).to(dt)
+            z = torch.randn(nh, w.group, d, generator=gen, device=device)
+            q[b, h0 * w.group:h1 * w.group] = (z + 0.5 * needle[:, None, :]).reshape(
+                nh * w.group, d).to(dt)
+    return K, V, q

@@ -199,6 +199,34 @@ def test_decode_tied_keys_more_clusters_than_one_key_pass():
     assert r["sel"][0].tolist() == list(range(2300))
 
 
+def _tie_to_pivots(w, k_r, k_e, n_tie):
+    """Every unit: the n_tie clusters ranked right after each pivot (the
+    K_r-th and the (K_r + K_e)-th ranked cluster of the exact group key) get
+    the pivot's centroid, so each pivot's histogram bin holds more than 64
+    keys (one wave's worth) but at most 256, all tied with the pivot."""
+    _, _, q = synth.gen_batch(w)
+    G = w.group
+
+    def mutate(idx):
+        c = idx["centroids"]
+        for u in range(c.shape[0]):
+            b, h = divmod(u, w.n_kv_heads)
+            Q = q[b, h * G:(h + 1) * G].astype(np.float64).sum(axis=0)
+            order = np.lexsort((np.arange(c.shape[1]), -(c[u].astype(np.float64) @ Q)))
+            for m in (k_r, k_r + k_e):
+                piv = order[m - 1]
+                c[u, order[m:m + n_tie]] = c[u, piv]
+    return mutate
+
+
+@pytest.mark.parametrize("w,k_r,k_e", [(SMALL, 9, 88), (LARGE_C, 300, 2000)],
+                         ids=["one-key-pass", "two-key-passes"])
+def test_decode_pivot_bins_beyond_one_wave(w, k_r, k_e):
+    r = _run(w, k_r, k_e, n_iters=1, mutate=_tie_to_pivots(w, k_r, k_e, 100))
+    assert r["mism"] == 0
+    assert r["err"] <= TOL["bf16"]
+
+
 def test_decode_graph_replay_matches_eager():
     """A decode call captured in a HIP graph and replayed several times, with
     eager decode calls of another query between the replays, gives the eager
