@@ -215,9 +215,13 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
                            : make_uint4(0, 0, 0, 0);
     }
 
-    uint32_t s1[NTL], s2[NTL];
+    // ~511 held in a vector register: with the code in a scalar register,
+    // mask and code then fit one v_and_or_b32 (one scalar operand)
+    uint32_t hi_mask;
+    asm volatile("v_mov_b32 %0, 0xfffffe00" : "=v"(hi_mask));
+    float s1[NTL], s2[NTL];
 #pragma unroll
-    for (int t = 0; t < NTL; t++) s1[t] = s2[t] = 0u;
+    for (int t = 0; t < NTL; t++) s1[t] = s2[t] = 0.f;
     // one 32-row tile: 8 k-steps of the dot products and the folded constants
     auto sweep = [&](int m, f32x16_t* acc) {
 #pragma unroll
@@ -246,35 +250,42 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
     // r = 32 m + 8 (i / 4) + 4 (lane >> 5) + (i % 4); the code 511 - r goes in
     // the low 9 bits
     auto fold = [&](int m, const f32x16_t* acc) {
-      const int cm = 511 - 32 * m - 4 * (lane >> 5);
+      // the code of row r is 511 - r = 511 ^ r. Bit 2 of r is 4 (lane >> 5)
+      // and the other bits are wave-uniform, so the fold uses the uniform
+      // part 511 ^ (r - 4 (lane >> 5)) (bit 2 set for every row of a lane,
+      // which leaves the lane's order unchanged) and the lane's bit 2 is
+      // fixed once after the sweep.
+      const int cm = 511 - 32 * m;  // (the codes live in scalar registers)
       // two scores at a time: the best of {s1, e0, e1} is a three-input max,
       // the second best of {s1, s2, e0, e1} the larger of s2 and the median
-      // of {s1, e0, e1} (s1 >= s2 holds throughout)
+      // of {s1, e0, e1} (s1 >= s2 holds throughout). The encoded values are
+      // non-negative floats, whose order is the order of their bit patterns,
+      // so the float three-input max and median instructions serve.
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const uint32_t code = (uint32_t)(cm - (8 * (i >> 2) + (i & 3)));  // row i + 1: code - 1
 #pragma unroll
         for (int t = 0; t < NTL; t++) {
-          const uint32_t e0 = (__float_as_uint(acc[t][i]) & ~511u) | code;
-          const uint32_t e1 = (__float_as_uint(acc[t][i + 1]) & ~511u) | (code - 1u);
-          const uint32_t md = max(min(e0, e1), min(max(e0, e1), s1[t]));  // v_med3_u32
-          s1[t] = max(max(s1[t], e0), e1);                                // v_max3_u32
-          s2[t] = max(s2[t], md);
+          const float e0 = __uint_as_float((__float_as_uint(acc[t][i]) & hi_mask) | code);
+          const float e1 = __uint_as_float((__float_as_uint(acc[t][i + 1]) & hi_mask) | (code - 1u));
+          const float md = __builtin_amdgcn_fmed3f(e0, e1, s1[t]);
+          s1[t] = fmaxf(fmaxf(s1[t], e0), e1);
+          s2[t] = fmaxf(s2[t], md);
         }
       }
     };
     // two accumulator sets: tile m + 1 is swept while tile m is folded (nm
-    // is even; the last pass sweeps tile nm - 1 again and discards it); then
-    // the next block's points are requested, in flight while the labels are
-    // written
+    // is even); the last two tiles are peeled so that no tile is swept
+    // twice. Then the next block's points are requested, in flight while the
+    // labels are written.
     f32x16_t accA[NTL], accB[NTL];
 
     sweep(0, accA);
 #pragma unroll 1
-    for (int m = 0; m < nm; m += 2) {
+    for (int m = 0; m < nm - 2; m += 2) {
       sweep(m + 1, accB);
       fold(m, accA);
-      sweep(min(m + 2, nm - 1), accA);
+      sweep(m + 2, accA);
       fold(m + 1, accB);
       // interleave: each MFMA followed by a few epilogue instructions
 #pragma unroll
@@ -283,6 +294,14 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
     }
+    sweep(nm - 1, accB);
+    fold(nm - 2, accA);
+#pragma unroll
+    for (int i = 0; i < 18; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    fold(nm - 1, accB);
     int jn = 0;
     if (lane == 0) jn = atomicAdd(&next_unit, 1);
     const int pn = unit_base(__builtin_amdgcn_readfirstlane(jn));
@@ -290,9 +309,12 @@ __global__ __launch_bounds__(BT, 1) void assign_bf16_kernel(Geom g, const void* 
 
 #pragma unroll
     for (int t = 0; t < NTL; t++) {
-      const uint32_t o1 = __shfl_xor(s1[t], 32, 64), o2 = __shfl_xor(s2[t], 32, 64);
-      const uint32_t b1 = max(s1[t], o1);
-      const uint32_t b2 = max(min(s1[t], o1), max(s2[t], o2));
+      // the lane's bit 2 of the row code (rows 4 (lane >> 5) apart)
+      const uint32_t h4 = (uint32_t)(lane >> 5) << 2;
+      const uint32_t c1 = __float_as_uint(s1[t]) ^ h4, c2 = __float_as_uint(s2[t]) ^ h4;
+      const uint32_t o1 = __shfl_xor(c1, 32, 64), o2 = __shfl_xor(c2, 32, 64);
+      const uint32_t b1 = max(c1, o1);
+      const uint32_t b2 = max(min(c1, o1), max(c2, o2));
       const int p = pb + 32 * t + (lane & 31);
       if (lane < 32 && p < n) {
         const float a1 = __uint_as_float(b1 & ~511u), a2 = __uint_as_float(b2 & ~511u);
