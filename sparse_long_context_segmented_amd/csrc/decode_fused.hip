@@ -298,6 +298,28 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       }
     }
   };
+  // C > CL: the keys of pass p straight into registers, each load issued
+  // unconditionally (index clamped into the unit's key row, padded to a
+  // multiple of 4; keys at i >= n are ignored), so that the next pass's
+  // loads can be in flight while this pass is processed
+  auto key_load = [&](int p, uint4* k4) {
+    const int c0 = p * CL, n = min(CL, C - c0);
+    const int last = ((n + 3) & ~3) - 4;
+#pragma unroll
+    for (int r = 0; r < KPT / 4; r++)
+      k4[r] = *reinterpret_cast<const uint4*>(keyg + c0 + min(4 * (tid + r * NT), last));
+  };
+  auto count_keys = [&](int p, const uint4* k4) {
+    const int n = min(CL, C - p * CL);
+#pragma unroll
+    for (int r = 0; r < KPT / 4; r++) {
+      const int i = 4 * (tid + r * NT);
+      const uint32_t kk[4] = {k4[r].x, k4[r].y, k4[r].z, k4[r].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        if (i + e < n) atomicAdd(&hist[bin_of(kk[e], lo, inv)], 1);
+    }
+  };
   // re-stage pass p for a later scan (C > CL only); leaves keys ready in LDS
   auto restage = [&](int p) {
     uint4 k4[KPT / 4];
@@ -326,10 +348,17 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     inv = hi > lo ? (float)NBINS / (hi - lo) : 0.f;
     __syncthreads();  // histogram cleared
     stage_store(0, k4, true);
+    if constexpr (BIG) {
+      // passes 1 .. NP-1: pass p + 1 loads while pass p is counted
+      uint4 kb[KPT / 4];
+      key_load(1, k4);
 #pragma unroll 1
-    for (int p = 1; p < NP; p++) {
-      stage_load(p, k4);
-      stage_store(p, k4, true);
+      for (int p = 1; p < NP; p += 2) {
+        key_load(min(p + 1, NP - 1), kb);
+        count_keys(p, k4);
+        key_load(min(p + 2, NP - 1), k4);
+        if (p + 1 < NP) count_keys(p + 1, kb);
+      }
     }
   }
   __syncthreads();
@@ -421,13 +450,14 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   }
 
   // ---- 1d. keys of the pivot bins -------------------------------------------
-  auto cand_scan = [&](int p) {
+  // pass p's keys: from LDS (one pass) or from registers k4r (C > CL)
+  auto cand_scan = [&](int p, const uint4* k4r) {
     const int n = min(CL, C - p * CL);
 #pragma unroll
     for (int r = 0; r < KPT / 4; r++) {
       const int i = 4 * (tid + r * NT);
       if (i >= n) continue;
-      const uint4 k4 = *reinterpret_cast<const uint4*>(keys + i);
+      const uint4 k4 = k4r ? k4r[r] : *reinterpret_cast<const uint4*>(keys + i);
       const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
       int bns[4];
 #pragma unroll
@@ -453,14 +483,19 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     }
   };
   // (two code paths, so that the common one issues no global load and the
-  // compiler puts no wait for outstanding loads in it)
-  if (NP == 1) {
-    cand_scan(0);
+  // compiler puts no wait for outstanding loads in it; with C > CL pass
+  // p + 1's keys load while pass p is scanned)
+  if constexpr (!BIG) {
+    cand_scan(0, nullptr);
   } else {
+    uint4 ka[KPT / 4], kb[KPT / 4];
+    key_load(0, ka);
 #pragma unroll 1
-    for (int p = 0; p < NP; p++) {
-      restage(p);
-      cand_scan(p);
+    for (int p = 0; p < NP; p += 2) {
+      key_load(min(p + 1, NP - 1), kb);
+      cand_scan(p, ka);
+      key_load(min(p + 2, NP - 1), ka);
+      if (p + 1 < NP) cand_scan(p + 1, kb);
     }
   }
   __syncthreads();
