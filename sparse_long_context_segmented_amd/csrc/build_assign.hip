@@ -436,11 +436,18 @@ __global__ __launch_bounds__(AT, 2) void assign_f32_kernel(Geom g, const void* _
 
 // ---------------------------------------------------------------------------
 // Exact fallback: one wave per listed point, float64 distances to every
-// centroid of its segment, lowest id on ties.
+// centroid of their segment, lowest id on ties. Lane l takes centroids l,
+// l + 64, ...: it reads its centroid's row with 16-byte loads, and the point
+// (in LDS, float64) is read back one broadcast value per dimension; each
+// distance is summed in dimension order.
 template <int DT>
 __global__ __launch_bounds__(256) void assign_fix_kernel(Geom g, const void* __restrict__ K,
                                                           const void* __restrict__ cent,
                                                           BuildWs ws) {
+  constexpr int ES = DT == WI_BF16 ? 2 : 4;  // bytes per element
+  constexpr int NV = D * ES / 16;            // 16-byte vectors per row
+  constexpr int EPV = 16 / ES;               // elements per vector
+  __shared__ double xs[4][D];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int cnt = ws.amb[0];
   const int nw = gridDim.x * 4;
@@ -452,35 +459,45 @@ __global__ __launch_bounds__(256) void assign_fix_kernel(Geom g, const void* __r
     const int i = (int)(loc % g.seg_len);
     const int Cs = seg_c(g, s), cb = seg_cbase(g, s);
     const uint8_t* xr = kptr<DT>(K, g, u, seg_first(g, s) + i);
-    // lane holds dims lane and lane + 64; broadcast with shuffles
-    double xa, xb;
+    // the point into LDS (lane holds dims lane and lane + 64)
     if constexpr (DT == WI_BF16) {
       const uint16_t* x16 = reinterpret_cast<const uint16_t*>(xr);
-      xa = (double)__uint_as_float(((uint32_t)x16[lane]) << 16);
-      xb = (double)__uint_as_float(((uint32_t)x16[lane + 64]) << 16);
+      xs[wv][lane] = (double)__uint_as_float(((uint32_t)x16[lane]) << 16);
+      xs[wv][lane + 64] = (double)__uint_as_float(((uint32_t)x16[lane + 64]) << 16);
     } else {
       const float* x32 = reinterpret_cast<const float*>(xr);
-      xa = (double)x32[lane];
-      xb = (double)x32[lane + 64];
+      xs[wv][lane] = (double)x32[lane];
+      xs[wv][lane + 64] = (double)x32[lane + 64];
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     double bd = INFINITY;
     int bi = 0x7FFFFFFF;
     const int rounds = (Cs + 63) / 64;
     for (int rd = 0; rd < rounds; rd++) {
       const int c = rd * 64 + lane;
       const bool ok = c < Cs;
-      const int cc = ok ? c : 0;
+      const uint4* crow = reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint8_t*>(cent) + ((int64_t)u * g.C + cb + (ok ? c : 0)) * D * ES);
+      uint4 cv[NV];
+#pragma unroll
+      for (int v = 0; v < NV; v++) cv[v] = crow[v];
       double acc = 0.0;
-      for (int t = 0; t < D; t++) {
-        const double xt = __shfl(t < 64 ? xa : xb, t & 63, 64);
-        double ct;
-        if constexpr (DT == WI_BF16)
-          ct = (double)__uint_as_float(((uint32_t) reinterpret_cast<const uint16_t*>(cent)
-                                            [((int64_t)u * g.C + cb + cc) * D + t]) << 16);
-        else
-          ct = (double)reinterpret_cast<const float*>(cent)[((int64_t)u * g.C + cb + cc) * D + t];
-        const double dl = xt - ct;
-        acc = __builtin_fma(dl, dl, acc);
+#pragma unroll
+      for (int v = 0; v < NV; v++) {
+        const uint32_t w[4] = {cv[v].x, cv[v].y, cv[v].z, cv[v].w};
+#pragma unroll
+        for (int k = 0; k < EPV; k++) {
+          const int t = v * EPV + k;
+          double ct;
+          if constexpr (DT == WI_BF16)
+            ct = (double)__uint_as_float((k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16));
+          else
+            ct = (double)__uint_as_float(w[k]);
+          const double dl = xs[wv][t] - ct;
+          acc = __builtin_fma(dl, dl, acc);
+        }
       }
       if (ok && acc < bd) {  // c grows within a lane: strict < keeps the lowest id
         bd = acc;
@@ -497,6 +514,10 @@ __global__ __launch_bounds__(256) void assign_fix_kernel(Geom g, const void* __r
       }
     }
     if (lane == 0) ws.label[pid] = bi;
+    // the next point rewrites this wave's row of xs only after every lane read it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 

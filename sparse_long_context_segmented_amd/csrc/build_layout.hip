@@ -9,7 +9,9 @@
 // id order; its members fill the first n_c slots in ascending position and
 // the rest of its last block holds token -1 and zero data, as do all blocks
 // past block_off[C]. Value sums are float64 sums over members in ascending
-// position, rounded to float32.
+// position, rounded to float32. Four workgroups share a segment (cluster c
+// goes to workgroup c % 4); the member list is staged in LDS and each wave
+// keeps 16 rows in flight, so the copy is not bound by dependent round trips.
 #include "wi_internal.h"
 
 namespace wi {
@@ -17,6 +19,7 @@ namespace {
 
 constexpr int LT = 512;
 constexpr int LW = LT / 64;
+constexpr int LP = 4;  // workgroups per segment: cluster c goes to workgroup c % LP
 
 // Per unit: first block of every segment, and blocks used by the unit.
 __global__ __launch_bounds__(256) void seg_scan_kernel(Geom g, BuildWs ws) {
@@ -57,7 +60,9 @@ __global__ __launch_bounds__(LT) void layout_kernel(Geom g, const void* __restri
   constexpr int RPW = 64 / LPR;                    // rows per wave step
   __shared__ int lbo[MAX_K + 1];
   __shared__ int wsum[LW + 1];
-  const int gs = blockIdx.x, u = gs / g.n_seg, s = gs % g.n_seg;
+  __shared__ int smemb[MAX_SEG];  // the segment's members, cluster order
+  __shared__ int scoff[MAX_K], scsz[MAX_K];
+  const int gs = blockIdx.x, u = gs / g.n_seg, s = gs % g.n_seg, part = blockIdx.y;
   const int n = seg_n(g, s), Cs = seg_c(g, s), cb = seg_cbase(g, s);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t pbase = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len;
@@ -73,6 +78,13 @@ __global__ __launch_bounds__(LT) void layout_kernel(Geom g, const void* __restri
   const int seg_b0 = ws.seg_bbase[gs];
   const int T = g.T;
 
+  // the member list and the clusters' sizes and offsets into LDS, so that a
+  // row's address is one LDS read away
+  for (int i = tid; i < n; i += LT) smemb[i] = memb[i];
+  if (tid < Cs) {
+    scsz[tid] = csz[tid];
+    scoff[tid] = coff[tid];
+  }
   // block offsets of the segment's clusters (Cs <= 512 <= LT)
   {
     const int nb = tid < Cs ? (csz[tid] + T - 1) / T : 0;
@@ -96,10 +108,10 @@ __global__ __launch_bounds__(LT) void layout_kernel(Geom g, const void* __restri
     __syncthreads();
     if (tid < Cs) {
       lbo[tid] = wsum[wv] + x - nb;
-      bf.block_off[(int64_t)u * (g.C + 1) + cb + tid] = seg_b0 + wsum[wv] + x - nb;
+      if (part == 0) bf.block_off[(int64_t)u * (g.C + 1) + cb + tid] = seg_b0 + wsum[wv] + x - nb;
     }
     if (tid == 0) lbo[Cs] = wsum[LW];
-    if (tid == 0 && s == g.n_seg - 1)
+    if (tid == 0 && s == g.n_seg - 1 && part == 0)
       bf.block_off[(int64_t)u * (g.C + 1) + g.C] = ws.unit_used[u];
     __syncthreads();
   }
@@ -109,55 +121,89 @@ __global__ __launch_bounds__(LT) void layout_kernel(Geom g, const void* __restri
   int32_t* stok = bf.slot_token + (int64_t)u * g.cap * T;
   const int rsub = lane / LPR, rl = lane % LPR;
 
-  // K/V rows into slots, padding slots zero / -1
-  for (int c = wv; c < Cs; c += LW) {
-    const int nc = csz[c];
+  // K/V rows into slots, padding slots zero / -1; a wave moves RU row steps
+  // (RU * RPW rows) per round, all loads of a round issued before its stores
+  constexpr int RU = 4;
+  for (int c = part + LP * wv; c < Cs; c += LP * LW) {
+    const int nc = scsz[c];
     const int nsl = (lbo[c + 1] - lbo[c]) * T;
     const int64_t slot0 = (int64_t)(seg_b0 + lbo[c]) * T;
-    for (int j = rsub; j < nsl; j += RPW) {
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-      int tok = -1;
-      if (j < nc) {
-        const int64_t pos = first + memb[coff[c] + j];
-        tok = (int)pos;
-        kv = reinterpret_cast<const uint4*>(Kb + pos * strow)[rl];
-        vv = reinterpret_cast<const uint4*>(Vb + pos * strow)[rl];
+    const int* cm = smemb + scoff[c];
+    for (int j0 = 0; j0 < nsl; j0 += RU * RPW) {
+      uint4 kv[RU], vv[RU];
+      int tok[RU];
+#pragma unroll
+      for (int q = 0; q < RU; q++) {
+        const int j = j0 + q * RPW + rsub;
+        kv[q] = vv[q] = make_uint4(0, 0, 0, 0);
+        tok[q] = -1;
+        if (j < nc) {
+          const int64_t pos = first + cm[j];
+          tok[q] = (int)pos;
+          kv[q] = reinterpret_cast<const uint4*>(Kb + pos * strow)[rl];
+          vv[q] = reinterpret_cast<const uint4*>(Vb + pos * strow)[rl];
+        }
       }
-      reinterpret_cast<uint4*>(kout + (slot0 + j) * RB)[rl] = kv;
-      reinterpret_cast<uint4*>(vout + (slot0 + j) * RB)[rl] = vv;
-      if (rl == 0) stok[slot0 + j] = tok;
+#pragma unroll
+      for (int q = 0; q < RU; q++) {
+        const int j = j0 + q * RPW + rsub;
+        if (j < nsl) {
+          reinterpret_cast<uint4*>(kout + (slot0 + j) * RB)[rl] = kv[q];
+          reinterpret_cast<uint4*>(vout + (slot0 + j) * RB)[rl] = vv[q];
+          if (rl == 0) stok[slot0 + j] = tok[q];
+        }
+      }
     }
   }
 
-  // value sums: one wave per cluster, lane owns dims 2*lane, 2*lane+1
-  for (int c = wv; c < Cs; c += LW) {
-    const int nc = csz[c];
-    const int m0 = coff[c];
+  // value sums: one wave per cluster, lane owns dims 2*lane, 2*lane+1; the
+  // rows of VU members are requested together, then added in ascending
+  // position
+  constexpr int VU = 16;
+  for (int c = part + LP * wv; c < Cs; c += LP * LW) {
+    const int nc = scsz[c];
+    const int* cm = smemb + scoff[c];
     double a0 = 0.0, a1 = 0.0;
-    for (int m = 0; m < nc; m++) {
-      const int64_t pos = first + memb[m0 + m];
-      if constexpr (DT == WI_BF16) {
-        const uint32_t w = reinterpret_cast<const uint32_t*>(Vb + pos * strow)[lane];
-        a0 += (double)__uint_as_float(w << 16);
-        a1 += (double)__uint_as_float(w & 0xFFFF0000u);
-      } else {
-        const float2 f = reinterpret_cast<const float2*>(Vb + pos * strow)[lane];
-        a0 += (double)f.x;
-        a1 += (double)f.y;
+    for (int m0 = 0; m0 < nc; m0 += VU) {
+      float x0[VU], x1[VU];
+#pragma unroll
+      for (int r = 0; r < VU; r++) {
+        x0[r] = x1[r] = 0.f;
+        if (m0 + r < nc) {
+          const int64_t pos = first + cm[m0 + r];
+          if constexpr (DT == WI_BF16) {
+            const uint32_t w = reinterpret_cast<const uint32_t*>(Vb + pos * strow)[lane];
+            x0[r] = __uint_as_float(w << 16);
+            x1[r] = __uint_as_float(w & 0xFFFF0000u);
+          } else {
+            const float2 f = reinterpret_cast<const float2*>(Vb + pos * strow)[lane];
+            x0[r] = f.x;
+            x1[r] = f.y;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < VU; r++) {
+        if (m0 + r < nc) {
+          a0 += (double)x0[r];
+          a1 += (double)x1[r];
+        }
       }
     }
     reinterpret_cast<float2*>(bf.value_sum)[((int64_t)u * g.C + cb + c) * (D / 2) + lane] =
         make_float2((float)a0, (float)a1);
   }
 
-  // global cluster ids of the segment's points
-  for (int i = tid; i < n; i += LT) bf.assign[pbase + i] = cb + ws.label[pbase + i];
+  // global cluster ids of the segment's points (this workgroup's quarter)
+  for (int i = n * part / LP + tid; i < n * (part + 1) / LP; i += LT)
+    bf.assign[pbase + i] = cb + ws.label[pbase + i];
 
-  // this segment's share of the unused tail blocks
+  // this workgroup's share of the unused tail blocks
   {
     const int64_t used = ws.unit_used[u];
     const int64_t tail = g.cap - used;
-    const int64_t t0 = used + tail * s / g.n_seg, t1 = used + tail * (s + 1) / g.n_seg;
+    const int64_t sh = (int64_t)s * LP + part, nsh = (int64_t)g.n_seg * LP;
+    const int64_t t0 = used + tail * sh / nsh, t1 = used + tail * (sh + 1) / nsh;
     for (int64_t sl = t0 * T + wv * RPW + rsub; sl < t1 * T; sl += LW * RPW) {
       reinterpret_cast<uint4*>(kout + sl * RB)[rl] = make_uint4(0, 0, 0, 0);
       reinterpret_cast<uint4*>(vout + sl * RB)[rl] = make_uint4(0, 0, 0, 0);
@@ -165,8 +211,8 @@ __global__ __launch_bounds__(LT) void layout_kernel(Geom g, const void* __restri
     }
   }
 
-  // steady zone copies (first segment's workgroup)
-  if (s == 0) {
+  // steady zone copies (first segment's first workgroup)
+  if (s == 0 && part == 0) {
     uint8_t* sk = reinterpret_cast<uint8_t*>(bf.steady_k) + (int64_t)u * g.n_st * RB;
     uint8_t* sv = reinterpret_cast<uint8_t*>(bf.steady_v) + (int64_t)u * g.n_st * RB;
     for (int j = wv * RPW + rsub; j < g.n_st; j += LW * RPW) {
@@ -187,11 +233,11 @@ hipError_t launch_layout(const Geom& g, const void* K, const void* V, const wi_i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.dtype == WI_BF16)
-    WI_LAUNCH(K_LAYOUT, layout_kernel<WI_BF16>, dim3(g.U * g.n_seg), dim3(LT), 0, s, g, K, V, b,
-                       ws);
+    WI_LAUNCH(K_LAYOUT, layout_kernel<WI_BF16>, dim3(g.U * g.n_seg, LP), dim3(LT), 0, s, g, K, V,
+              b, ws);
   else
-    WI_LAUNCH(K_LAYOUT, layout_kernel<WI_F32>, dim3(g.U * g.n_seg), dim3(LT), 0, s, g, K, V, b,
-                       ws);
+    WI_LAUNCH(K_LAYOUT, layout_kernel<WI_F32>, dim3(g.U * g.n_seg, LP), dim3(LT), 0, s, g, K, V,
+              b, ws);
   return hipGetLastError();
 }
 

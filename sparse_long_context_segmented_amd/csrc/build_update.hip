@@ -144,6 +144,28 @@ __global__ __launch_bounds__(UT) void sort_update_kernel(Geom g, const void* __r
     if (nc == 0) continue;
     double a0 = 0.0, a1 = 0.0;
     int m = m0;
+    // the rows of 16 members are requested together, then added in order
+    for (; m + 16 <= m1; m += 16) {
+      float x0[16], x1[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const uint8_t* row = kp<DT>(K, g, u, first + memb[m + r]);
+        if constexpr (DT == WI_BF16) {
+          const uint32_t w = reinterpret_cast<const uint32_t*>(row)[lane];
+          x0[r] = __uint_as_float(w << 16);
+          x1[r] = __uint_as_float(w & 0xFFFF0000u);
+        } else {
+          const float2 f = reinterpret_cast<const float2*>(row)[lane];
+          x0[r] = f.x;
+          x1[r] = f.y;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        a0 += (double)x0[r];
+        a1 += (double)x1[r];
+      }
+    }
     for (; m + 4 <= m1; m += 4) {
       float x0[4], x1[4];
 #pragma unroll
