@@ -2,7 +2,8 @@
 // blog section 2.1 segmented_kmeans sketch; gist.science summary,
 // "Technische Samenvatting" 2A: centroids are cluster averages).
 //
-// One workgroup (16 waves) per segment:
+// Two workgroups (16 waves each) per segment; both sort, each computes the
+// means of half the clusters (c % 2), and the first writes the lists:
 //   1. stable counting sort of the segment's points by cluster: per-wave
 //      histograms in LDS, a scan over (cluster, wave), then each wave places
 //      its points in position order; equal labels inside a 64-point round are
@@ -20,6 +21,7 @@ namespace {
 
 constexpr int UT = 1024;
 constexpr int UW = UT / 64;
+constexpr int UP = 2;  // workgroups per segment: both sort, cluster c's mean goes to c % UP
 
 template <int DT>
 __device__ __forceinline__ const uint8_t* kp(const void* K, const Geom& g, int u, int64_t pos) {
@@ -37,11 +39,12 @@ __global__ __launch_bounds__(UT) void sort_update_kernel(Geom g, const void* __r
   __shared__ int memb[MAX_SEG];
   __shared__ int coff[MAX_K + 1];
   __shared__ int wsum[UW + 1];
-  const int gs = blockIdx.x, u = gs / g.n_seg, s = gs % g.n_seg;
+  const int gs = blockIdx.x, u = gs / g.n_seg, s = gs % g.n_seg, part = blockIdx.y;
   const int n = seg_n(g, s), Cs = seg_c(g, s), cb = seg_cbase(g, s);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t pbase = (int64_t)u * g.n_idx + (int64_t)s * g.seg_len;
   const int* lab = ws.label + pbase;
+  if (part != 0 && !do_update) return;  // only the lists are wanted
 
   for (int i = tid; i < UW * MAX_K; i += UT) (&hist[0][0])[i] = 0;
   __syncthreads();
@@ -83,8 +86,10 @@ __global__ __launch_bounds__(UT) void sort_update_kernel(Geom g, const void* __r
         hist[w][tid] = base;
         base += t2;
       }
-      csize[(int64_t)u * g.C + cb + tid] = tot;
-      ws.cl_off[(int64_t)u * g.C + cb + tid] = excl;
+      if (part == 0) {
+        csize[(int64_t)u * g.C + cb + tid] = tot;
+        ws.cl_off[(int64_t)u * g.C + cb + tid] = excl;
+      }
     }
   }
   __syncthreads();
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(UT) void sort_update_kernel(Geom g, const void* __r
     for (int o = 32; o > 0; o >>= 1) nb += __shfl_xor(nb, o, 64);
     if (lane == 0) wsum[wv] = nb;
     __syncthreads();
-    if (tid == 0) {
+    if (tid == 0 && part == 0) {
       int sb = 0;
       for (int w = 0; w < UW; w++) sb += wsum[w];
       ws.seg_blocks[gs] = sb;
@@ -129,7 +134,8 @@ __global__ __launch_bounds__(UT) void sort_update_kernel(Geom g, const void* __r
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
-  for (int i = tid; i < n; i += UT) ws.members[pbase + i] = memb[i];
+  if (part == 0)
+    for (int i = tid; i < n; i += UT) ws.members[pbase + i] = memb[i];
   if (tid <= Cs) {
     if (tid == Cs) coff[Cs] = n;
   }
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(UT) void sort_update_kernel(Geom g, const void* __r
   if (!do_update) return;
   // means: one wave per cluster, lane owns dims 2*lane, 2*lane+1
   const int64_t first = seg_first(g, s);
-  for (int c = wv; c < Cs; c += UW) {
+  for (int c = part + UP * wv; c < Cs; c += UP * UW) {
     const int m0 = coff[c], m1 = coff[c + 1];
     const int nc = m1 - m0;
     if (nc == 0) continue;
@@ -216,11 +222,11 @@ __global__ __launch_bounds__(UT) void sort_update_kernel(Geom g, const void* __r
 hipError_t launch_sort_update(const Geom& g, const void* K, void* cent, int32_t* csize,
                               const BuildWs& ws, bool do_update, hipStream_t s) {
   if (g.dtype == WI_BF16)
-    WI_LAUNCH(K_SORT_UPDATE, sort_update_kernel<WI_BF16>, dim3(g.U * g.n_seg), dim3(UT), 0, s, g, K,
-                       cent, csize, ws, (int)do_update);
+    WI_LAUNCH(K_SORT_UPDATE, sort_update_kernel<WI_BF16>, dim3(g.U * g.n_seg, UP), dim3(UT), 0,
+              s, g, K, cent, csize, ws, (int)do_update);
   else
-    WI_LAUNCH(K_SORT_UPDATE, sort_update_kernel<WI_F32>, dim3(g.U * g.n_seg), dim3(UT), 0, s, g, K,
-                       cent, csize, ws, (int)do_update);
+    WI_LAUNCH(K_SORT_UPDATE, sort_update_kernel<WI_F32>, dim3(g.U * g.n_seg, UP), dim3(UT), 0, s,
+              g, K, cent, csize, ws, (int)do_update);
   return hipGetLastError();
 }
 
