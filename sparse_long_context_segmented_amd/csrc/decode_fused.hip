@@ -183,7 +183,8 @@ struct Lds {
   static constexpr int HIST = KEYS + CL * 4;                  // int[NBINS]
   static constexpr int CANDK = HIST + NBINS * 4;              // uint32[2][CAND_MAX]
   static constexpr int CANDI = CANDK + 2 * CAND_MAX * 4;      // int[2][CAND_MAX]
-  static constexpr int RTOK = CANDI + 2 * CAND_MAX * 4;       // int[NT + 4]
+  static constexpr int BINS = CANDI + 2 * CAND_MAX * 4;       // uint16[CL] histogram bin per key
+  static constexpr int RTOK = BINS + CL * 2;                  // int[NT + 4]
   static constexpr int RBLK = RTOK + (NT + 4) * 4;            // int[NT]
   static constexpr int EID = RBLK + NT * 4;                   // int[NT]
   static constexpr int ESZ = EID + NT * 4;                    // float[NT]
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   int* hist = reinterpret_cast<int*>(smem + L::HIST);
   uint32_t* candk = reinterpret_cast<uint32_t*>(smem + L::CANDK);
   int* candi = reinterpret_cast<int*>(smem + L::CANDI);
+  uint16_t* kbin = reinterpret_cast<uint16_t*>(smem + L::BINS);
   int* Rtok = reinterpret_cast<int*>(smem + L::RTOK);
   int* Rblk = reinterpret_cast<int*>(smem + L::RBLK);
   int* Eid = reinterpret_cast<int*>(smem + L::EID);
@@ -291,9 +293,15 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
         *reinterpret_cast<uint4*>(keys + i) = k4[r];
         if (count) {
           const uint32_t kk[4] = {k4[r].x, k4[r].y, k4[r].z, k4[r].w};
+          int bn[4];
 #pragma unroll
-          for (int e = 0; e < 4; e++)
-            if (i + e < n) atomicAdd(&hist[bin_of(kk[e], lo, inv)], 1);
+          for (int e = 0; e < 4; e++) {
+            bn[e] = bin_of(kk[e], lo, inv);
+            if (i + e < n) atomicAdd(&hist[bn[e]], 1);
+          }
+          // (pass 0's bins are kept for the candidate scan of a one-pass unit)
+          *reinterpret_cast<uint2*>(kbin + i) =
+              make_uint2((uint32_t)bn[0] | ((uint32_t)bn[1] << 16), (uint32_t)bn[2] | ((uint32_t)bn[3] << 16));
         }
       }
     }
@@ -332,6 +340,12 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   // ---- 1a.-1b. key range (from the score step) and histogram -----------------
   for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
   if (tid < 2) ncand[tid] = 0;
+  // candidate lists start as entries that never rank above a candidate (key
+  // 0, id INT_MAX), so the ranking can read them four at a time past nc
+  for (int i = tid; i < 2 * CAND_MAX; i += NT) {
+    candk[i] = 0u;
+    candi[i] = INT_MAX;
+  }
   {
     uint4 k4[KPT / 4];
     stage_load(0, k4);
@@ -457,14 +471,23 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     for (int r = 0; r < KPT / 4; r++) {
       const int i = 4 * (tid + r * NT);
       if (i >= n) continue;
-      const uint4 k4 = k4r ? k4r[r] : *reinterpret_cast<const uint4*>(keys + i);
-      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
       int bns[4];
+      if (k4r) {
+        const uint32_t kr[4] = {k4r[r].x, k4r[r].y, k4r[r].z, k4r[r].w};
 #pragma unroll
-      for (int e = 0; e < 4; e++) bns[e] = bin_of(kk[e], lo, inv);
+        for (int e = 0; e < 4; e++) bns[e] = bin_of(kr[e], lo, inv);
+      } else {
+        const uint2 bb = *reinterpret_cast<const uint2*>(kbin + i);
+        bns[0] = bb.x & 0xFFFF;
+        bns[1] = bb.x >> 16;
+        bns[2] = bb.y & 0xFFFF;
+        bns[3] = bb.y >> 16;
+      }
       const bool any = (bns[0] == b1) | (bns[1] == b1) | (bns[2] == b1) | (bns[3] == b1) |
                        (bns[0] == b2) | (bns[1] == b2) | (bns[2] == b2) | (bns[3] == b2);
       if (!any) continue;
+      const uint4 k4 = k4r ? k4r[r] : *reinterpret_cast<const uint4*>(keys + i);
+      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         if (i + e < n) {
@@ -501,8 +524,8 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   __syncthreads();
 
   // ---- 1e. pivots: waves 4t .. 4t + 3 rank the keys of target t's bin, one
-  // candidate per lane (candidate 64 (wv % 4) + lane); up to 64 candidates
-  // one wave compares through lane reads, more through LDS reads --------------
+  // candidate per lane (candidate 64 (wv % 4) + lane), comparing against
+  // four candidates per pair of LDS broadcast reads --------------------------
   const int nc0 = ncand[0], nc1 = ncand[1];
   {
     const int t = wv >> 2, qw = wv & 3;
@@ -513,20 +536,16 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       const uint32_t kk = i < nc ? candk[t * CAND_MAX + i] : 0u;
       const int id = i < nc ? candi[t * CAND_MAX + i] : INT_MAX;
       int rank = 0;
-      if (nc <= 64) {
-#pragma unroll 1
-        for (int j = 0; j < nc; j++) {
-          const uint32_t kj = (uint32_t)rdl((int)kk, j);
-          const int idj = rdl(id, j);
-          rank += (kj > kk) || (kj == kk && idj < id);
-        }
-      } else {
-#pragma unroll 1
-        for (int j = 0; j < nc; j++) {
-          const uint32_t kj = candk[t * CAND_MAX + j];
-          const int idj = candi[t * CAND_MAX + j];
-          rank += (kj > kk) || (kj == kk && idj < id);
-        }
+      const uint4* ck = reinterpret_cast<const uint4*>(candk + t * CAND_MAX);
+      const int4* ci = reinterpret_cast<const int4*>(candi + t * CAND_MAX);
+#pragma unroll 4
+      for (int j4 = 0; j4 < (nc + 3) / 4; j4++) {
+        const uint4 k4 = ck[j4];
+        const int4 i4 = ci[j4];
+        rank += (k4.x > kk) || (k4.x == kk && i4.x < id);
+        rank += (k4.y > kk) || (k4.y == kk && i4.y < id);
+        rank += (k4.z > kk) || (k4.z == kk && i4.z < id);
+        rank += (k4.w > kk) || (k4.w == kk && i4.w < id);
       }
       if (i < nc && rank == bneed[t] - 1) {
         pk[t] = kk;
