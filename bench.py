@@ -171,6 +171,20 @@ def main():
     wall = time.perf_counter() - t_start
     step_ms = ev0.elapsed_time(ev1) / a.steps
 
+    # per-step distribution: HIP events around each of the steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    for i in range(a.steps):
+        j = i % len(copies)
+        evs[i][0].record(stream)
+        wi.decode_attention(copies[j], dd, qt, out=outs[j], ws=wsd)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    step_pct = {"p10": round(float(np.percentile(per_step, 10)), 5),
+                "p50": round(float(np.percentile(per_step, 50)), 5),
+                "p90": round(float(np.percentile(per_step, 90)), 5)}
+
     # the same steps replayed from a HIP graph (one decode call per index copy,
     # captured once): launch overhead between the two kernels of a step
     graph = torch.cuda.CUDAGraph()
@@ -232,6 +246,7 @@ def main():
                    "seg_len": w.seg_len, "clusters_per_seg": w.clusters_per_seg,
                    "k_retrieve": k_r, "k_estimate": k_e_eff, "index_copies": len(copies)},
         "step_hbm_GBps": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+        "ms_per_step_bracketed": step_pct,
         "graph_replay": {"ms_per_step": round(graph_step_ms, 5),
                          "queries_per_s": round(w.batch / (graph_step_ms * 1e-3), 1)},
         "step_bytes": int(step_bytes),
