@@ -176,6 +176,11 @@ __device__ __forceinline__ float ex(float x) {
   else return expf(x);
 }
 
+// Own-cluster chunks whose item lists are gathered before their items run:
+// four (2048 clusters) when the lists fit in LDS (head groups of up to 4),
+// else one.
+constexpr int PASS_CHUNKS(int GS) { return GS <= 4 ? 4 : 1; }
+
 // ---- LDS layout -------------------------------------------------------------
 template <int GS>
 struct Lds {
@@ -184,12 +189,13 @@ struct Lds {
   static constexpr int CANDK = HIST + NBINS * 4;              // uint32[2][CAND_MAX]
   static constexpr int CANDI = CANDK + 2 * CAND_MAX * 4;      // int[2][CAND_MAX]
   static constexpr int BINS = CANDI + 2 * CAND_MAX * 4;       // uint16[CL] histogram bin per key
-  static constexpr int RTOK = BINS + CL * 2;                  // int[NT + 4]
-  static constexpr int RBLK = RTOK + (NT + 4) * 4;            // int[NT]
-  static constexpr int EID = RBLK + NT * 4;                   // int[NT]
-  static constexpr int ESZ = EID + NT * 4;                    // float[NT]
-  static constexpr int ELOG = ESZ + NT * 4;                   // float[NT][GS]
-  static constexpr int PBUF = ELOG + NT * GS * 4;             // float[NW][PI_MAX][GS]
+  static constexpr int LN = NT * PASS_CHUNKS(GS);             // list capacity
+  static constexpr int RTOK = BINS + CL * 2;                  // int[LN + 4]
+  static constexpr int RBLK = RTOK + (LN + 4) * 4;            // int[LN]
+  static constexpr int EID = RBLK + LN * 4;                   // int[LN]
+  static constexpr int ESZ = EID + LN * 4;                    // float[LN]
+  static constexpr int ELOG = ESZ + LN * 4;                   // float[LN][GS]
+  static constexpr int PBUF = ELOG + LN * GS * 4;             // float[NW][PI_MAX][GS]
   static constexpr int QS = PBUF + NW * PI_MAX * GS * 4;          // query rows, GS x 128 x dtype
   static constexpr int END = QS + GS * D * 4;
   static constexpr int SACC = 0;                              // float[NW][GS][D]
@@ -620,16 +626,19 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
 #pragma unroll
   for (int g = 0; g < GS; g++) acc[g][0] = acc[g][1] = 0.f;
 
-  // one chunk of own clusters; the first is peeled off the loop, so that its
-  // code joins no path holding later chunks' loads (the compiler would
-  // otherwise place waits there that also cover the warm-up loads)
-  auto chunk = [&](const int ch) {
-    // (i) zones of the chunk's clusters and the chunk's item lists. The
-    // first chunk's cluster data was loaded at kernel start; a later chunk
-    // loads its own inside its branch. Each branch consumes what it loads,
-    // so the compiler places no wait for other outstanding loads after it.
-    int nR = 0, nRtok = 0, nE = 0;
-    auto setup = [&](int n, int blk, const f32x4_t* sl) {
+  // own clusters in passes of PASS_CHUNKS(GS) chunks of NT: the item lists of
+  // a pass's chunks are gathered (appended) before its items run. The first
+  // pass is peeled off the loop, so that its code joins no path holding later
+  // passes' loads (the compiler would otherwise place waits there that also
+  // cover the warm-up loads)
+  constexpr int PC = PASS_CHUNKS(GS);
+  auto chunk = [&](const int c0) {
+    // (i) zones of the pass's clusters and its item lists. Chunk 0's cluster
+    // data was loaded at kernel start; a later chunk loads its own inside its
+    // branch. Each branch consumes what it loads, so the compiler places no
+    // wait for other outstanding loads after it.
+    int nR = 0, nRtok = 0, nE = 0;  // running list lengths over the pass
+    auto setup = [&](int ch, int n, int blk, const f32x4_t* sl) {
       const int k = ch * NT + tid;
       const int id = own_id(k);
       const bool ok = k < n_own && id < C;
@@ -644,36 +653,41 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       const int v3[3] = {(int)rT, rT ? n : 0, (int)eT};
       int off3[3], tot3[3];
       block_scan<3>(v3, off3, tot3, scan_lds);
-      nR = tot3[0];
-      nRtok = tot3[1];
-      nE = tot3[2];
       if (rT) {
-        Rtok[off3[0]] = off3[1];
-        Rblk[off3[0]] = blk;
+        Rtok[nR + off3[0]] = nRtok + off3[1];
+        Rblk[nR + off3[0]] = blk;
       }
       if (eT) {
-        Eid[off3[2]] = id;
-        Esz[off3[2]] = (float)n;
-        float* el = Elog + off3[2] * GS;
+        Eid[nE + off3[2]] = id;
+        Esz[nE + off3[2]] = (float)n;
+        float* el = Elog + (nE + off3[2]) * GS;
 #pragma unroll
         for (int g4 = 0; g4 < GS / 4; g4++) *reinterpret_cast<f32x4_t*>(el + 4 * g4) = sl[g4];
       }
+      nR += tot3[0];
+      nRtok += tot3[1];
+      nE += tot3[2];
     };
-    if (ch == 0) {
-      setup(sz0, blk0, sl0);
-    } else {
-      const int k = ch * NT + tid;
-      const int id = own_id(k);
-      const int idc = k < n_own && id < C ? id : 0;
-      const int n = a.size[uC + idc];
-      const int blk = a.block_off[(int64_t)u * (C + 1) + idc];
-      f32x4_t sl[GS / 4];
-      const f32x4_t* sp = reinterpret_cast<const f32x4_t*>(a.S + (uC + idc) * GS);
+    const int c1 = min(c0 + PC, n_chunks);
+#pragma unroll 1
+    for (int ch = c0; ch < c1; ch++) {
+      if (ch == 0) {
+        setup(0, sz0, blk0, sl0);
+      } else {
+        const int k = ch * NT + tid;
+        const int id = own_id(k);
+        const int idc = k < n_own && id < C ? id : 0;
+        const int n = a.size[uC + idc];
+        const int blk = a.block_off[(int64_t)u * (C + 1) + idc];
+        f32x4_t sl[GS / 4];
+        const f32x4_t* sp = reinterpret_cast<const f32x4_t*>(a.S + (uC + idc) * GS);
 #pragma unroll
-      for (int g4 = 0; g4 < GS / 4; g4++) sl[g4] = sp[g4];
-      setup(n, blk, sl);
+        for (int g4 = 0; g4 < GS / 4; g4++) sl[g4] = sp[g4];
+        setup(ch, n, blk, sl);
+      }
     }
     __syncthreads();
+    const int ch = c0;  // (the first pass holds the steady tokens)
     // token items: the own steady tokens (first chunk only), then the chunk's
     // retrieved tokens; estimation items: the chunk's estimation clusters.
     // Wave wv takes token blocks (TB tokens) wv, wv + NW, ... and estimation
@@ -870,7 +884,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   };
   chunk(0);
 #pragma unroll 1
-  for (int ch = 1; ch < n_chunks; ch++) chunk(ch);
+  for (int c0 = PC; c0 < n_chunks; c0 += PC) chunk(c0);
 
   // the warm-up values are consumed (the condition never holds: K_r >= 0)
   const uint32_t warm = w4[0] ^ w4[1] ^ w4[2] ^ w4[3] ^ wk[0] ^ wk[1] ^ wk[2] ^ wk[3] ^ wst;
