@@ -176,10 +176,10 @@ __device__ __forceinline__ float ex(float x) {
   else return expf(x);
 }
 
-// Own-cluster chunks whose item lists are gathered before their items run:
-// four (2048 clusters) when the lists fit in LDS (head groups of up to 4),
-// else one.
-constexpr int PASS_CHUNKS(int GS) { return GS <= 4 ? 4 : 1; }
+// Own-cluster chunks whose item lists are gathered before their items run, as
+// many as the lists' LDS allows: four (2048 clusters) for head groups of up
+// to 4, two for up to 8, else one.
+constexpr int PASS_CHUNKS(int GS) { return GS <= 4 ? 4 : (GS <= 8 ? 2 : 1); }
 
 // ---- LDS layout -------------------------------------------------------------
 template <int GS>
