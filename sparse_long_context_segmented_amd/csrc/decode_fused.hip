@@ -29,11 +29,12 @@
 //     within that bin. The
 //     sizes, block offsets and estimation logits of the workgroup's first
 //     512 own clusters are loaded at kernel start, behind the selection.
-//  2. Own clusters, 512 at a time: one block scan gives each retrieved
-//     cluster with members its first token among the chunk's retrieved
-//     tokens, and each estimation cluster with members its slot. Retrieved
-//     tokens are read straight from the cluster-contiguous 2 KB blocks (the
-//     first n_c rows of the cluster: fragments skipped).
+//  2. Own clusters, 512 at a time: one block scan per 512 gives each
+//     retrieved cluster with members its first token among the retrieved
+//     tokens, and each estimation cluster with members its slot; the lists
+//     of up to PASS_CHUNKS(GS) such chunks are appended before their items
+//     run. Retrieved tokens are read straight from the cluster-contiguous 2 KB
+//     blocks (the first n_c rows of the cluster: fragments skipped).
 //  3. Items, in blocks of 32 tokens (16 for fp32) and 16 estimation clusters;
 //     wave v takes blocks v, v + 8, ... and runs with no workgroup barrier.
 //     A lane finds its token's row by binary search over the retrieved
