@@ -78,7 +78,7 @@ def measured_traffic(workload):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
+        print(f"bench.py: measures one GPU only; --gpus {a.gpus} is not supported "
               "(the path shards by KV head / sequence with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
