@@ -189,6 +189,20 @@ def test_decode_tied_keys(k_r, k_e):
     assert sel[0].tolist() == list(range(k_r + min(k_e, r["C"] - k_r)))
 
 
+@pytest.mark.parametrize("G", [7, 16])
+def test_decode_gathered_lists_over_several_passes(G):
+    """More than 8192 clusters per unit and two workgroups per unit: each
+    workgroup owns about 4357 clusters (nine 512-cluster chunks), so the item
+    lists are gathered over several passes of two chunks (groups of 5-8
+    heads) or one (larger groups)."""
+    w = synth.custom(240 + G, "bf16", 1, 2 * G, 2, 68 + 17 * 1024 + 10, 1024, 512, n_needles=4,
+                     anisotropic=(G == 7))
+    r = _run(w, 300, 2000, n_iters=1, wg=2)
+    assert r["C"] == 8714
+    assert r["mism"] == 0
+    assert r["err"] <= TOL["bf16"]
+
+
 def test_decode_tied_keys_more_clusters_than_one_key_pass():
     def tie(idx):
         c = idx["centroids"]
