@@ -240,7 +240,21 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   __shared__ int rneed, s_last;
   __shared__ float cden[MAX_G];
 
-  const int w = blockIdx.x, u = blockIdx.y;
+  // XCD-aware placement: the dispatcher deals consecutive workgroups round
+  // robin to the 8 XCDs, so with a unit count that is a multiple of 8 the
+  // linear id L = 8 slot + x maps to unit (slot / W) 8 + x, workgroup
+  // slot % W: all W workgroups of a unit run on one XCD and share its L2
+  // copy of the unit's keys, scores and cluster data (a bijection on the grid)
+  int w, u;
+  if ((gridDim.y & 7) == 0) {
+    const int L = (int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x;
+    const int slot = L >> 3;
+    u = (slot / (int)gridDim.x) * 8 + (L & 7);
+    w = slot % (int)gridDim.x;
+  } else {
+    w = blockIdx.x;
+    u = blockIdx.y;
+  }
   const int b = u / a.H, h = u % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
