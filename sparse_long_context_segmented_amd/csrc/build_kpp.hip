@@ -280,7 +280,21 @@ template <int DT>
 __global__ __launch_bounds__(NT, DT == WI_BF16 ? 8 : 5) void kpp_round_kernel(Geom g, const void* __restrict__ K,
                                                         void* __restrict__ cent, BuildWs ws,
                                                         int nsl, int r) {
-  const int gs = blockIdx.y, slice = blockIdx.x;
+  // XCD-aware placement: the dispatcher deals consecutive workgroups round
+  // robin to the 8 XCDs; with a segment count that is a multiple of 8,
+  // linear id L = 8 q + x runs segment (q / nsl) 8 + x, slice q % nsl, so the
+  // slices of a segment share one L2 for the data every one of them reads to
+  // derive the pick (slice sums, the owner slice's weights, the picked row)
+  int gs, slice;
+  if ((gridDim.y & 7) == 0) {
+    const int L = (int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x;
+    const int q = L >> 3;
+    gs = (q / (int)gridDim.x) * 8 + (L & 7);
+    slice = q % (int)gridDim.x;
+  } else {
+    gs = blockIdx.y;
+    slice = blockIdx.x;
+  }
   const int s = gs % g.n_seg;
   const int n = seg_n(g, s);
   if (slice * NT >= n) return;
