@@ -475,15 +475,16 @@ int wio_decode(const wio_desc *d, const wio_ddesc *dd, const float *centroids,
     /* Score ([blog] 2.2: query the wave index for cluster ids). Reading:
      * one selection per KV head, keyed by the sum over its query heads of
      * <q_h, centroid>; this ranks like the scaled logit sum. The key is that
-     * sum computed in float64 (exact for bf16 data) and rounded once to
-     * float32, the precision the ranking is taken in; equal keys go to the
-     * lower cluster id. */
+     * sum in float64 -- exact for bf16 data, whose products and short sums
+     * are exact there -- and equal keys go to the lower cluster id. The
+     * pages fix no precision for the ranking, so the oracle ranks on the
+     * exact group score. */
     ranked *rk = (ranked *)malloc(sizeof(ranked) * (size_t)C);
     for (int64_t c = 0; c < C; c++) {
       double g = 0.0;
       for (int j = 0; j < G; j++)
         g += dot64(qg + (size_t)j * D, centroids + ((size_t)u * C + c) * D, D);
-      rk[c].g = (double)(float)g;
+      rk[c].g = g;
       rk[c].id = (int32_t)c;
       if (gkey) gkey[(size_t)u * C + c] = g;
     }

@@ -34,28 +34,36 @@ def rel_err(out: np.ndarray, ref: np.ndarray) -> float:
     return float((num / den).max())
 
 
+def near_tie(a: float, b: float) -> bool:
+    """Ranking keys within the 1e-5 relative window (logit units, floor 1)."""
+    return abs(a - b) <= 1e-5 * max(abs(a), abs(b), 1.0)
+
+
 def check_selection(sel_gpu: np.ndarray, gkey: np.ndarray, k_r: int) -> int:
     """Compare a selection (rank order) with the exact group scores.
 
-    The ranking key is the float64 group score rounded to float32, larger
-    first, lower id on equal keys; the GPU computes the same key. Returns the
-    number of positions where the GPU order differs from that ranking; every
-    such difference must be a near-tie (exact keys within 1e-5 relative).
+    The oracle ranks on the exact (float64) group score, larger first, lower
+    id on equal scores. The GPU ranks on that score rounded to float32, so two
+    clusters whose scores round alike go by id there. Every position where the
+    GPU order differs from the exact ranking must pair two clusters whose exact
+    scores are a near-tie (within 1e-5 relative); the number of such positions
+    is returned (and printed by the callers). The selected ids must be
+    distinct, and the retrieval and estimation sets may differ from the exact
+    ones only by near-tied swaps across their boundaries.
     """
     U, M = sel_gpu.shape
     mism = 0
     for u in range(U):
-        key32 = gkey[u].astype(np.float32).astype(np.float64)
-        order = np.lexsort((np.arange(len(key32)), -key32))[:M]
+        key = gkey[u].astype(np.float64)
+        order = np.lexsort((np.arange(len(key)), -key))[:M]
+        assert len(set(sel_gpu[u].tolist())) == M, f"unit {u}: repeated ids"
         if np.array_equal(order, sel_gpu[u]):
             continue
         diff = np.nonzero(order != sel_gpu[u])[0]
         mism += len(diff)
         for i in diff:
-            a, b = gkey[u][order[i]], gkey[u][sel_gpu[u][i]]
-            assert abs(a - b) <= 1e-5 * max(abs(a), abs(b), 1.0), (u, i, a, b)
-        # set-level: R and E sets must be valid under near-ties as well
-        assert len(set(sel_gpu[u].tolist())) == M
+            a, b = key[order[i]], key[sel_gpu[u][i]]
+            assert near_tie(a, b), (u, int(i), float(a), float(b))
     return mism
 
 

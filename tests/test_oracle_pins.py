@@ -354,10 +354,36 @@ def test_select_matches_lexsort(orc):
     for u in range(d.batch * d.n_kv_heads):
         b, h = divmod(u, d.n_kv_heads)
         g = (q[b, h * G:(h + 1) * G].astype(np.float64) @ idx["centroids"][u].astype(np.float64).T).sum(0)
-        # ranking key: the float64 group score rounded to float32
-        order = np.lexsort((np.arange(C), -g.astype(np.float32).astype(np.float64)))
+        # ranking key: the exact group score (bf16 products and their short
+        # sums are exact in float64), larger first, lower id on ties
+        order = np.lexsort((np.arange(C), -g))
         assert np.array_equal(res["sel"][u], order[:14])
         assert np.allclose(res["gkey"][u], g, rtol=1e-12, atol=1e-12)
+
+
+def test_select_exact_key_breaks_float32_ties(orc):
+    """Two centroids whose group scores differ by far less than float32
+    resolution: the exact score decides their order (the higher-id cluster,
+    whose score is larger by |Q_t| 2^-40, ranks first), not the cluster id."""
+    w, d, K, V, q = _small("bf16")
+    idx = orc.build(d, K, V)
+    ns, C, cap, T = orc.sizes(d)
+    G = 3
+    c_lo, c_hi = 2, 7
+    cent = idx["centroids"]
+    for u in range(d.batch * d.n_kv_heads):
+        b, h = divmod(u, d.n_kv_heads)
+        Q = q[b, h * G:(h + 1) * G].astype(np.float64).sum(0)
+        t = int(np.argmax(np.abs(Q)))
+        cent[u, c_lo, t] = 0.0
+        cent[u, c_hi] = cent[u, c_lo]
+        cent[u, c_hi, t] = np.float32(math.copysign(2.0 ** -40, Q[t]))  # exact in bf16
+        g = (q[b, h * G:(h + 1) * G].astype(np.float64) @ cent[u].astype(np.float64).T).sum(0)
+        assert g[c_hi] > g[c_lo] and np.float32(g[c_hi]) == np.float32(g[c_lo])
+    res = orc.decode(d, 6, C, 0, idx, q)
+    for u in range(d.batch * d.n_kv_heads):
+        sel = res["sel"][u].tolist()
+        assert sel.index(c_hi) == sel.index(c_lo) - 1
 
 
 def test_decode_equals_bruteforce_tripartite(orc):
