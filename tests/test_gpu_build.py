@@ -120,161 +120,3 @@ def test_build_deterministic():
     b = index_to_host(wi.build_index(gd, kt, vt))
     torch.cuda.synchronize()
     assert_index_equal(a, b)
-
-
-def _full_size_sampled(w, units):
-    """Build and decode a whole workload in one call each (the benchmark's
-    launch configuration); the oracle rebuilds the sampled units from the
-    same seeded inputs, whose index must match bit-for-bit and whose decode
-    outputs must be within the bf16 tolerance."""
-    from parity import rel_err, upload_q
-    print(f"[full-size parity] {w.name} units {units}", flush=True)
-    K, V, q = synth.gen_batch(w)
-    gd, _ = descs(w)
-    kt, vt = upload_kv(K, V, w.dtype)
-    ix = wi.build_index(gd, kt, vt)
-    k_r, k_e = w.budgets()
-    dd = wi.DecodeDesc(w.n_q_heads, k_r, k_e, 0.0)
-    out = wi.decode_attention(ix, dd, upload_q(q, w.dtype))
-    torch.cuda.synchronize()
-    out = out.cpu().numpy()
-    got = index_to_host(ix, units)  # the sampled units only, in order
-    del kt, vt, ix
-    H = w.n_kv_heads
-    # the oracle builds only the sampled units, over the leading sequences
-    # that hold them (so each keeps its (sequence, head) random stream)
-    bmax = max(units) // H + 1
-    od = oracle.make_desc("bf16", bmax, H, w.n_ctx, n_iters=w.n_iters)
-    ref = oracle.build(od, K[:bmax], V[:bmax], units=units)
-    ref = {k: v[list(units)] for k, v in ref.items()}
-    assert_index_equal(got, ref)
-    od1 = oracle.make_desc("bf16", 1, 1, w.n_ctx, n_iters=w.n_iters)
-    for i, u in enumerate(units):
-        b, h = divmod(u, H)
-        sub = {k: v[i:i + 1] for k, v in ref.items()}
-        qu = q[b:b + 1, h * w.group:(h + 1) * w.group]
-        r = oracle.decode(od1, w.group, k_r, k_e, sub, qu)
-        e = rel_err(out[b:b + 1, h * w.group:(h + 1) * w.group], r["out"])
-        print(f"  unit (b={b}, h={h}): index exact, decode rel err {e:.3e}", flush=True)
-        assert e <= 2e-3
-
-
-@pytest.mark.slow
-def test_build_and_decode_llama8b_128k_sampled_units():
-    _full_size_sampled(synth.WORKLOADS[1], (0, 5))
-
-
-@pytest.mark.slow
-def test_build_and_decode_llama8b_128k_batch8_sampled_units():
-    """64 units in one call (4 select/attend workgroups per unit)."""
-    _full_size_sampled(synth.WORKLOADS[2], (2, 14))
-
-
-@pytest.mark.slow
-def test_build_and_decode_qwen7b_256k_batch4_sampled_units():
-    """16 384 clusters per unit (two LDS passes of keys), 7 query heads per KV
-    head, anisotropic keys."""
-    _full_size_sampled(synth.WORKLOADS[3], (2, 5))
-
-
-def _check_unit_structure(got, Ku, Vu, n_ctx, seg_len, k, T, n_sink=4, n_local=64):
-    """Properties of one unit's index that hold at any size, checked without
-    rebuilding it: sizes count the assignment, every token is assigned inside
-    its own segment's cluster range, clusters occupy ceil(size/T) blocks in id
-    order holding their members in ascending position (then -1 / zero pad),
-    the blocks hold the tokens' keys and values, each non-empty centroid is
-    the float64 mean of its members rounded to float32 then bf16, and each
-    value sum is the float64 sum of its members' values rounded to float32."""
-    from oracle.brute import bf16, partition
-    a = got["assign"][0]
-    sz, bo, st = got["sizes"][0], got["block_off"][0], got["slot_token"][0]
-    C = len(sz)
-    assert np.array_equal(sz, np.bincount(a, minlength=C))
-    for p0, n, cs, cb in partition(n_ctx, seg_len, k, n_sink, n_local):
-        seg = a[p0 - n_sink: p0 - n_sink + n]
-        assert seg.min() >= cb and seg.max() < cb + cs, (p0, cb)
-    nb = (sz + T - 1) // T
-    assert bo[0] == 0 and np.array_equal(np.diff(bo), nb)
-    order = np.argsort(a, kind="stable")           # members by cluster, ascending position
-    slots = np.repeat(bo[:-1] * T, sz) + (np.arange(len(a)) - np.repeat(np.cumsum(sz) - sz, sz))
-    assert np.array_equal(st[slots], order + n_sink)
-    pad = np.ones(len(st), bool)
-    pad[slots] = False
-    assert np.all(st[pad] == -1)
-    kb = got["kblk"][0].reshape(-1, 128)
-    vb = got["vblk"][0].reshape(-1, 128)
-    assert np.array_equal(kb[slots], Ku[order + n_sink])
-    assert np.array_equal(vb[slots], Vu[order + n_sink])
-    assert not kb[pad].any() and not vb[pad].any()
-    nz = np.nonzero(sz)[0]
-    starts = (np.cumsum(sz) - sz)[nz]
-    ks = np.add.reduceat(Ku[order + n_sink].astype(np.float64), starts, axis=0)
-    mean = bf16((ks / sz[nz, None]).astype(np.float32))
-    assert np.array_equal(got["centroids"][0][nz].view(np.uint32), mean.view(np.uint32))
-    vs = np.add.reduceat(Vu[order + n_sink].astype(np.float64), starts, axis=0)
-    assert np.array_equal(got["vsum"][0][nz].view(np.uint32), vs.astype(np.float32).view(np.uint32))
-    assert not got["vsum"][0][sz == 0].any()
-    steady = list(range(n_sink)) + list(range(n_ctx - n_local, n_ctx))
-    assert np.array_equal(got["steady_k"][0][:len(steady)], Ku[steady])
-    assert np.array_equal(got["steady_v"][0][:len(steady)], Vu[steady])
-
-
-@pytest.mark.slow
-@pytest.mark.timeout(600)
-def test_build_and_decode_llama8b_1m_one_layer_sampled_unit():
-    """One layer (layer 3 of 32, so the layer id enters the random stream) of
-    the 1M-token Llama3-8B-1048K-shaped model: all 8 KV heads built and decoded
-    in one call each (65 536 clusters per unit in 128 segments). For unit
-    (0, 0): the oracle's k-means++ and Lloyd steps rerun on three segments
-    (first, middle, short last) must give the same centroids and assignment
-    bit-for-bit; the whole unit's index must have the structure above; and the
-    oracle's decode over that index must agree with the GPU's output within
-    the bf16 tolerance."""
-    from concurrent.futures import ThreadPoolExecutor
-    from oracle.brute import partition
-    from parity import rel_err, upload_q
-    w, layer = synth.WORKLOADS[4], 3
-    H, T = w.n_kv_heads, 8
-    print(f"[full-size parity] {w.name} layer {layer}", flush=True)
-    with ThreadPoolExecutor(4) as ex:
-        parts = list(ex.map(lambda h: synth.gen_unit(w, 0, layer, h), range(H)))
-    K = np.stack([p[0] for p in parts])[None]
-    V = np.stack([p[1] for p in parts])[None]
-    q = np.concatenate([p[2] for p in parts], axis=0)[None]
-    del parts
-    gd, _ = descs(w, layer=layer)
-    kt, vt = upload_kv(K, V, w.dtype)
-    ix = wi.build_index(gd, kt, vt)
-    k_r, k_e = w.budgets()
-    dd = wi.DecodeDesc(w.n_q_heads, k_r, k_e, 0.0)
-    out = wi.decode_attention(ix, dd, upload_q(q, w.dtype))
-    torch.cuda.synchronize()
-    out = out.cpu().numpy()
-    got = index_to_host(ix, (0,))
-    del kt, vt, ix
-    torch.cuda.empty_cache()
-    Ku, Vu = K[0, 0], V[0, 0]
-    del K, V
-    print("  GPU build + decode done; checking unit (0, 0)", flush=True)
-    _check_unit_structure(got, Ku, Vu, w.n_ctx, w.seg_len, w.clusters_per_seg, T)
-    segs = partition(w.n_ctx, w.seg_len, w.clusters_per_seg)
-    assert len(segs) == 128 and segs[-1][1] < w.seg_len
-    for s in (0, 64, 127):
-        p0, n, cs, cb = segs[s]
-        X = Ku[p0: p0 + n]
-        picks = oracle.kmeanspp(X, cs, seed=0, b=0, l=layer, h=0, s=s)
-        Cs = X[picks]
-        a = oracle.assign(X, Cs)
-        for t in range(w.n_iters):
-            if t > 0:
-                a = oracle.assign(X, Cs)
-            Cs, _ = oracle.update(X, a, Cs, "bf16")
-        assert np.array_equal(got["centroids"][0][cb: cb + cs].view(np.uint32),
-                              Cs.view(np.uint32)), s
-        assert np.array_equal(got["assign"][0][p0 - 4: p0 - 4 + n], a + cb), s
-        print(f"  segment {s}: centroids and assignment exact", flush=True)
-    od1 = oracle.make_desc("bf16", 1, 1, w.n_ctx, n_iters=w.n_iters, layer_id=layer)
-    r = oracle.decode(od1, w.group, k_r, k_e, got, q[:1, :w.group])
-    e = rel_err(out[:1, :w.group], r["out"])
-    print(f"  unit (b=0, h=0): decode rel err {e:.3e}", flush=True)
-    assert e <= 2e-3
