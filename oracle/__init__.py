@@ -20,14 +20,45 @@ _SRC = os.path.join(_HERE, "wi_oracle.c")
 F32, BF16 = 0, 1
 
 
+def _host_has_fma() -> bool:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("flags"):
+                    return " fma " in line + " "
+    except OSError:
+        pass
+    return False
+
+
+def gcc_command(src: str, out: str) -> list:
+    """gcc line for the oracle: scalar code, no FMA contraction of separate
+    multiplies and adds. The explicit fma()/fmaf() calls are correctly
+    rounded either way; -mfma (where the host has it) only lets gcc emit the
+    instruction instead of a libm call."""
+    fma = ["-mfma"] if _host_has_fma() else []
+    return ["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            *fma, "-fPIC", "-shared", src, "-o", out, "-lm"]
+
+
+def _flags() -> str:
+    return " ".join(a for a in gcc_command("SRC", "OUT") if a not in ("SRC", "OUT"))
+
+
+def _built_for_this_host() -> bool:
+    stamp = _SO + ".flags"
+    return os.path.exists(stamp) and open(stamp).read() == _flags()
+
+
 def compile_oracle(force: bool = False) -> str:
-    """Compile the oracle with gcc: scalar code, no FMA contraction."""
-    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+    """Compile the oracle with gcc (see gcc_command)."""
+    if (force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC)
+            or not _built_for_this_host()):
         tmp = _SO + f".tmp{os.getpid()}"
-        subprocess.check_call([
-            "gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off",
-            "-fno-fast-math", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        subprocess.check_call(gcc_command(_SRC, tmp))
         os.replace(tmp, _SO)
+        with open(_SO + ".flags", "w") as f:
+            f.write(_flags())
     return _SO
 
 
