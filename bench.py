@@ -42,11 +42,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b-128k-b1")
-    ap.add_argument("--instances", type=int, default=16,
+    ap.add_argument("--instances", type=int, default=32,
                     help="index copies the steps rotate over")
     ap.add_argument("--build-reps", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="bound on the oracle's timed CPU work")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="bound on the oracle's timed decode loop")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--wg", type=int, default=0,
                     help="fused-kernel workgroups per (sequence, KV head); 0 = automatic")
@@ -158,13 +158,16 @@ def main():
     wsd = torch.empty(wi.decode_sizes(desc, dd), dtype=torch.uint8, device=dev)
     outs = [torch.empty(w.batch, w.n_q_heads, 128, dtype=torch.float32, device=dev)
             for _ in range(len(copies))]
+    # warm-up on copies 0 .. warmup-1; the timed steps continue from copy
+    # `warmup`, so a warm-up copy is read again only after R - warmup other
+    # copies (R x the step's bytes far exceeds the 256 MB last-level cache)
     for i in range(a.warmup):
         wi.decode_attention(copies[i % len(copies)], dd, qt, out=outs[i % len(copies)], ws=wsd)
     torch.cuda.synchronize()
     ev0.record(stream)
     t_start = time.perf_counter()
     for i in range(a.steps):
-        j = i % len(copies)
+        j = (a.warmup + i) % len(copies)
         wi.decode_attention(copies[j], dd, qt, out=outs[j], ws=wsd)
     ev1.record(stream)
     torch.cuda.synchronize()
@@ -257,7 +260,12 @@ def main():
     }
 
     if not a.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, K, V, q, k_r, k_e, a.cpu_seconds)
+        # every unit of the layer when the oracle builds them in about half a
+        # minute on the host (the 128K batch-1 layer); otherwise the units of
+        # the first sequence, scaled to the whole batch
+        U1 = w.n_kv_heads if w.batch > 1 else U
+        res["cpu_baseline"] = cpu_baseline(w, K, V, q, k_r, k_e, a.cpu_seconds,
+                                           units=list(range(U1)))
     print(json.dumps(res), flush=True)
 
 
@@ -300,6 +308,10 @@ def model_bench(a, w):
             for name, ms in wi.timing_stop():
                 bk.setdefault(name, []).append(ms)
         build_ms.append(ev0.elapsed_time(ev1))
+        if l == L - 1 and not a.no_cpu:
+            # unit (b=0, h=0) of the last layer, for the oracle's baseline
+            host0 = (K[:1, :1].float().cpu().numpy(), V[:1, :1].float().cpu().numpy(),
+                     q[:1, :w.group].float().cpu().numpy())
         del K, V
         indexes.append(ix)
         qs.append(q)
@@ -379,44 +391,75 @@ def model_bench(a, w):
                              "frac": round(flops / (assign_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                              "ms_per_launch": round(assign_ms, 4)}},
         "gen_ms_per_layer": round(float(np.mean(gen_ms)), 1),
-        "cpu_baseline": None,
-        "cpu_baseline_note": "not run for the 32-layer model: the oracle builds one 1M-token "
-                             "unit in over a minute; the 128K default run carries it",
     }
+    if not a.no_cpu:
+        # one unit, (b=0, h=0) of the last layer: with a single KV head its
+        # random stream is that unit's, so the oracle builds exactly it
+        import dataclasses
+        w1 = dataclasses.replace(w, n_kv_heads=1, n_q_heads=w.group, layers=1)
+        res["cpu_baseline"] = cpu_baseline(w1, *host0, k_r, k_e, a.cpu_seconds, units=[0],
+                                           layer=L - 1, units_per_step=L * U,
+                                           queries_per_step=w.batch * L)
+        del host0
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(w, K, V, q, k_r, k_e, seconds):
-    """The oracle, untuned, on a bounded sample: one KV head (unit h = 0) of the
-    same workload, built once and decoded repeatedly for about `seconds`;
-    a decode step of the full layer is that unit's time x (units per step)."""
+def cpu_baseline(w, K, V, q, k_r, k_e, seconds, units, layer=0, units_per_step=None,
+                 queries_per_step=None):
+    """The oracle, untuned, on the host cores, on a bounded sample of the same
+    workload: the sampled units (b, h) of one layer are built in one oracle
+    call (OpenMP over the (unit, segment) jobs) and then decoded in one call
+    (OpenMP over the units), repeatedly for about `seconds`. K, V: host arrays
+    [B, H, N, 128] holding at least the sampled units' sequences. A decode
+    step covers units_per_step units (default: every unit of the layer); when
+    the sample holds fewer, the time is scaled by units_per_step / sample and
+    marked extrapolated (units are independent). value = queries_per_step
+    (default: the batch) / step time."""
     import oracle
     oracle.compile_oracle()
-    cores = oracle.num_threads()
-    od = oracle.make_desc(w.dtype, 1, 1, w.n_ctx, seg_len=w.seg_len,
-                          clusters_per_seg=w.clusters_per_seg, n_iters=w.n_iters)
-    K1, V1 = K[:1, :1], V[:1, :1]
+    threads = oracle.num_threads()
+    H, G = w.n_kv_heads, w.group
+    U = units_per_step or w.batch * H
+    bmax = max(units) // H + 1
+    od = oracle.make_desc(w.dtype, bmax, H, w.n_ctx, seg_len=w.seg_len,
+                          clusters_per_seg=w.clusters_per_seg, n_iters=w.n_iters,
+                          layer_id=layer)
+    ns = oracle.sizes(od)[0]
     t0 = time.perf_counter()
-    idx = oracle.build(od, K1, V1)
+    idx = oracle.build(od, K[:bmax], V[:bmax], units=units)
     build_s = time.perf_counter() - t0
-    q1 = q[:1, :w.group]
+    sub = {k: np.ascontiguousarray(v[list(units)]) for k, v in idx.items()}
+    del idx
+    # the sampled units' query heads, as one sequence of len(units) KV heads
+    qs = np.concatenate([q[u // H, (u % H) * G:(u % H + 1) * G] for u in units])[None]
+    od1 = oracle.make_desc(w.dtype, 1, len(units), w.n_ctx, seg_len=w.seg_len,
+                           clusters_per_seg=w.clusters_per_seg, n_iters=w.n_iters)
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.decode(od, w.group, k_r, k_e, idx, q1)
+        oracle.decode(od1, G * len(units), k_r, k_e, sub, qs)
         n += 1
         if time.perf_counter() - t0 > seconds:
             break
-    per_unit = (time.perf_counter() - t0) / n
-    units = w.batch * w.n_kv_heads
-    step = per_unit * units
-    return {"value": round(w.batch / step, 2), "unit": "queries/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"unit (b=0, h=0) of {units}: oracle build once ({build_s:.1f} s) "
-                      f"and {n} decode steps; step = unit time x {units}",
-            "decode_ms_per_unit": round(per_unit * 1e3, 2),
-            "build_s_per_unit": round(build_s, 2),
-            "build_s_layer_extrapolated": round(build_s * units, 1)}
+    sample_step = (time.perf_counter() - t0) / n
+    factor = U / len(units)
+    step = sample_step * factor
+    qps = queries_per_step or w.batch
+    return {"value": round(qps / step, 3),
+            "unit": "queries/s" if queries_per_step is None else "layer-queries/s",
+            "cores": min(threads, len(units)), "kind": "oracle",
+            "sample": (f"{len(units)} of {U} units per step (b, h) = "
+                       f"{[divmod(u, H) for u in units][:8]}{'...' if len(units) > 8 else ''}: "
+                       f"oracle build of those units in one call ({build_s:.1f} s, "
+                       f"{min(threads, len(units) * ns)} threads), then {n} decode calls over "
+                       f"them ({min(threads, len(units))} threads, one per unit)"
+                       + (f"; step time scaled x{factor:g} (extrapolated)" if factor != 1 else "")),
+            "extrapolated": factor != 1,
+            "decode_ms_per_step": round(step * 1e3, 3),
+            "decode_ms_sample": round(sample_step * 1e3, 3),
+            "build_s_sample": round(build_s, 2),
+            "build_s_per_step_units": round(build_s * factor, 1),
+            "threads_available": threads}
 
 
 if __name__ == "__main__":
