@@ -168,7 +168,8 @@ wi_status wi_decode_sizes(const wi_index_desc *desc,
  *   q            device [B][Hq][128] dtype
  *   out          device [B][Hq][128] float32 attention output
  *   Ranking: clusters of a unit are ranked by g_c = sum over the unit's query
- *   heads of <q_j, centroid_c> (float32), larger first, lower id on ties.
+ *   heads of <q_j, centroid_c>, computed exactly and rounded once to float32,
+ *   larger first, lower id on equal float32 keys.
  *   Ranks [0, K_r) form the retrieval zone R, the next
  *   min(K_e, C - K_r) ranks the estimation zone E. For each query head j:
  *     out_j = (sum_{i in steady + members(R)} e^{z_i} v_i

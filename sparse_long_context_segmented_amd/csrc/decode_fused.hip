@@ -46,8 +46,8 @@
 //     sum_i p_i v_i over token values and value sums VS_c).
 //  4. Merge: the waves' states are combined in a fixed order; the
 //     workgroup's (m, l, acc) per head is published with agent-coherent
-//     stores and one relaxed atomic counts arrivals; the last workgroup of
-//     the unit reads the W partials and writes
+//     stores and one agent-scope release atomic counts arrivals; the last
+//     workgroup of the unit acquires, reads the W partials and writes
 //     out = sum_w e^{m_w-M} acc_w / sum_w e^{m_w-M} l_w.
 // Every sum runs in a fixed order, so results are bit-reproducible.
 #include <climits>
@@ -941,12 +941,19 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       __hip_atomic_store(pw + g * PART + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  // the agent-coherent stores above are complete before the arrival count
+  // The arrival count is a release at agent scope: the workgroup barrier
+  // orders every thread's partial stores before thread 0's count, which makes
+  // them visible to the workgroup that observes the final count. That last
+  // workgroup then acquires at agent scope before any thread reads a partial
+  // (its barrier carries the acquire to the other threads).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&a.tix[u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             W - 1;
+  if (tid == 0) {
+    const bool last = __hip_atomic_fetch_add(&a.tix[u], 1, __ATOMIC_RELEASE,
+                                             __HIP_MEMORY_SCOPE_AGENT) == W - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
+  }
   __syncthreads();
   if (!s_last) return;
 
