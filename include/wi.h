@@ -198,6 +198,36 @@ wi_status wi_decode_attention(const wi_index_desc *desc,
                               int64_t exec_cap, void *ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* Largest decode workspace that wi_decode_attention_noalloc serves: 16 MiB
+ * (the five model shapes of this library need at most 11.5 MiB: 8 units of
+ * 65536 clusters, or 64 units of 8192). */
+#define WI_NOALLOC_SCRATCH_BYTES (16ull << 20)
+
+/* For callers that cannot allocate device memory or call an allocating
+ * routine: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same inputs, outputs and results as wi_decode_attention
+ * (same kernels); its workspace is a fixed device array of
+ * WI_NOALLOC_SCRATCH_BYTES inside the library instead of a caller buffer.
+ *   - Allocates nothing: no hipMalloc, hipFree or allocating library call.
+ *     On its first call on a device (that device current) it looks up that
+ *     device's copy of the array once (hipGetSymbolAddress) and keeps the
+ *     address; each GPU holds its copy until the process ends.
+ *   - Uses the calling thread's current device; `stream` must belong to it.
+ *   - Returns WI_E_WORKSPACE, before any HIP call, when wi_decode_sizes for
+ *     this call exceeds WI_NOALLOC_SCRATCH_BYTES.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (each call initialises what it reads): calls that may
+ *     overlap in time on one GPU (different streams, or different threads)
+ *     race and must be serialised by the caller. With the measurement hook
+ *     (wi_timing_start) on, its event creation is the hook's, not this
+ *     call's. */
+wi_status wi_decode_attention_noalloc(const wi_index_desc *desc,
+                                      const wi_decode_desc *ddesc,
+                                      const wi_index_bufs *bufs, const void *q,
+                                      float *out, int32_t *sel_ids,
+                                      int32_t *exec_tokens, int32_t *n_exec,
+                                      int64_t exec_cap, hipStream_t stream);
+
 /* Measurement hook. wi_timing_start() makes every kernel launch issued by
  * this library on the calling thread be bracketed by two HIP events recorded
  * on the launch's own stream, until wi_timing_stop(). wi_timing_stop()

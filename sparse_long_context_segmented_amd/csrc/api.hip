@@ -5,9 +5,17 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "wi_internal.h"
+
+// Device scratch of wi_decode_attention_noalloc: one copy per GPU, held from
+// the library's load until the process ends. In host code the name is only a
+// stand-in for the symbol; the device address is obtained per device with
+// hipGetSymbolAddress (see scratch_for_current_device) and only that address
+// is used.
+static __device__ __align__(256) unsigned char scratch[WI_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -347,15 +355,20 @@ wi_status wi_decode_sizes(const wi_index_desc* desc, const wi_decode_desc* ddesc
   return WI_OK;
 }
 
-wi_status wi_decode_attention(const wi_index_desc* desc, const wi_decode_desc* ddesc,
-                              const wi_index_bufs* bufs, const void* q, float* out,
-                              int32_t* sel_ids, int32_t* exec_tokens, int32_t* n_exec,
-                              int64_t exec_cap, void* ws, size_t ws_bytes, hipStream_t stream) {
-  wi::Geom g;
-  wi_status st = make_geom(desc, &g);
+}  // extern "C"
+
+namespace {
+
+// Host-side validation of a decode call (no HIP call); on success the
+// geometry, decode shape and workspace size are returned.
+wi_status validate_decode(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                          const wi_index_bufs* bufs, const void* q, const float* out,
+                          const int32_t* sel_ids, const int32_t* exec_tokens,
+                          const int32_t* n_exec, int64_t exec_cap, wi::Geom* g,
+                          DecodeShape* ds, int64_t* need) {
+  wi_status st = make_geom(desc, g);
   if (st != WI_OK) return st;
-  DecodeShape ds;
-  st = make_decode(g, ddesc, &ds);
+  st = make_decode(*g, ddesc, ds);
   if (st != WI_OK) return st;
   if (!bufs) return fail(WI_E_INVALID, "bufs is NULL");
   CHECK_PTR(bufs->centroids, "bufs->centroids");
@@ -364,7 +377,7 @@ wi_status wi_decode_attention(const wi_index_desc* desc, const wi_decode_desc* d
   CHECK_PTR(bufs->block_off, "bufs->block_off");
   CHECK_PTR(bufs->k_blocks, "bufs->k_blocks");
   CHECK_PTR(bufs->v_blocks, "bufs->v_blocks");
-  if (g.n_st > 0) {
+  if (g->n_st > 0) {
     CHECK_PTR(bufs->steady_k, "bufs->steady_k");
     CHECK_PTR(bufs->steady_v, "bufs->steady_v");
   }
@@ -377,15 +390,18 @@ wi_status wi_decode_attention(const wi_index_desc* desc, const wi_decode_desc* d
     if (exec_cap < 0) return fail(WI_E_INVALID, "exec_cap < 0");
     CHECK_PTR(bufs->slot_token, "bufs->slot_token");
   }
-  const int64_t need = carve_decode(g, ds, nullptr, nullptr);
-  if (!ws || (int64_t)ws_bytes < need)
-    return fail(WI_E_WORKSPACE, "workspace %zu bytes < %lld required", ws_bytes, (long long)need);
-  if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
+  *need = carve_decode(*g, *ds, nullptr, nullptr);
+  return WI_OK;
+}
+
+// The decode launches on a validated call, with the workspace at ws.
+wi_status run_decode(const wi::Geom& g, const DecodeShape& ds, const wi_index_bufs* bufs,
+                     const void* q, float* out, int32_t* sel_ids, int32_t* exec_tokens,
+                     int32_t* n_exec, int64_t exec_cap, void* ws, hipStream_t stream) {
   wi::DecodeWs w;
   carve_decode(g, ds, reinterpret_cast<uint8_t*>(ws), &w);
   wi::DecodeArgs a{&g, ds.Hq, ds.G, ds.GS, ds.K_r, ds.K_e, ds.W, ds.scale};
   const bool want_lists = sel_ids || exec_tokens || n_exec;
-
   CHECK_HIP(wi::launch_score(a, bufs->centroids, q, w, stream), "score");
   CHECK_HIP(wi::launch_fused(a, *bufs, q, out, w, want_lists, stream), "select/attend");
   if (want_lists)
@@ -394,6 +410,71 @@ wi_status wi_decode_attention(const wi_index_desc* desc, const wi_decode_desc* d
               "debug outputs");
   g_err[0] = 0;
   return WI_OK;
+}
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+wi_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(WI_E_UNSUPPORTED, "device ordinal %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(WI_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return WI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+wi_status wi_decode_attention(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                              const wi_index_bufs* bufs, const void* q, float* out,
+                              int32_t* sel_ids, int32_t* exec_tokens, int32_t* n_exec,
+                              int64_t exec_cap, void* ws, size_t ws_bytes, hipStream_t stream) {
+  wi::Geom g;
+  DecodeShape ds;
+  int64_t need = 0;
+  wi_status st = validate_decode(desc, ddesc, bufs, q, out, sel_ids, exec_tokens, n_exec,
+                                 exec_cap, &g, &ds, &need);
+  if (st != WI_OK) return st;
+  if (!ws || (int64_t)ws_bytes < need)
+    return fail(WI_E_WORKSPACE, "workspace %zu bytes < %lld required", ws_bytes, (long long)need);
+  if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
+  return run_decode(g, ds, bufs, q, out, sel_ids, exec_tokens, n_exec, exec_cap, ws, stream);
+}
+
+wi_status wi_decode_attention_noalloc(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                                      const wi_index_bufs* bufs, const void* q, float* out,
+                                      int32_t* sel_ids, int32_t* exec_tokens, int32_t* n_exec,
+                                      int64_t exec_cap, hipStream_t stream) {
+  wi::Geom g;
+  DecodeShape ds;
+  int64_t need = 0;
+  wi_status st = validate_decode(desc, ddesc, bufs, q, out, sel_ids, exec_tokens, n_exec,
+                                 exec_cap, &g, &ds, &need);
+  if (st != WI_OK) return st;
+  if (need > (int64_t)WI_NOALLOC_SCRATCH_BYTES)
+    return fail(WI_E_WORKSPACE,
+                "decode needs %lld bytes of scratch, more than the %lld-byte static array; "
+                "use wi_decode_attention with a caller workspace",
+                (long long)need, (long long)WI_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != WI_OK) return st;
+  return run_decode(g, ds, bufs, q, out, sel_ids, exec_tokens, n_exec, exec_cap, ws, stream);
 }
 
 }  // extern "C"

@@ -20,8 +20,9 @@ WI_F32, WI_BF16 = 0, 1
 STATUS = {0: "WI_OK", 1: "WI_E_INVALID", 2: "WI_E_UNSUPPORTED", 3: "WI_E_WORKSPACE",
           4: "WI_E_HIP"}
 EXPORTS = ("wi_index_sizes", "wi_build_index", "wi_decode_sizes", "wi_decode_attention",
-           "wi_status_str", "wi_last_error", "wi_timing_start", "wi_timing_stop",
-           "wi_kernel_name")
+           "wi_decode_attention_noalloc", "wi_status_str", "wi_last_error",
+           "wi_timing_start", "wi_timing_stop", "wi_kernel_name")
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class WIError(RuntimeError):
@@ -74,6 +75,8 @@ def lib():
         L.wi_decode_attention.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int64, P,
                                           ctypes.c_size_t, P]
         L.wi_decode_attention.restype = ctypes.c_int
+        L.wi_decode_attention_noalloc.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int64, P]
+        L.wi_decode_attention_noalloc.restype = ctypes.c_int
         L.wi_status_str.argtypes = [ctypes.c_int]
         L.wi_status_str.restype = ctypes.c_char_p
         L.wi_last_error.argtypes = []
@@ -209,6 +212,20 @@ def decode_attention(index: Index, ddesc: DecodeDesc, q: torch.Tensor,
                                      _ptr(q), _ptr(out), _ptr(sel_ids), _ptr(exec_tokens),
                                      _ptr(n_exec), exec_cap, _ptr(ws), ws.numel(),
                                      _stream(stream)))
+    return out
+
+
+def decode_attention_noalloc(index: Index, ddesc: DecodeDesc, q: torch.Tensor, out: torch.Tensor,
+                             sel_ids: torch.Tensor | None = None,
+                             exec_tokens: torch.Tensor | None = None,
+                             n_exec: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Run wi_decode_attention_noalloc: the caller passes every output; the
+    library's own static device scratch stands in for the workspace."""
+    bufs = index.bufs()
+    exec_cap = 0 if exec_tokens is None else exec_tokens.shape[-1]
+    _check(lib().wi_decode_attention_noalloc(
+        ctypes.byref(index.desc), ctypes.byref(ddesc), ctypes.byref(bufs), _ptr(q), _ptr(out),
+        _ptr(sel_ids), _ptr(exec_tokens), _ptr(n_exec), exec_cap, _stream(stream)))
     return out
 
 

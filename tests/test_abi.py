@@ -170,3 +170,38 @@ def test_decode_sizes_grow_with_budget(L):
         wi.decode_sizes(d, wi.DecodeDesc(32, 4096, 4096, 0.0))
     # any retrieval budget up to C is accepted
     assert wi.decode_sizes(d, wi.DecodeDesc(32, 8192, 0, 0.0)) > 0
+
+
+def test_noalloc_scratch_limit_matches_header():
+    hdr = open(os.path.join(ROOT, "include", "wi.h")).read()
+    m = re.search(r"#define WI_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == wi.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_workspace_beyond_static_maximum(L):
+    """128 units of 8192 clusters need more decode scratch than the static
+    array holds: rejected on the host, before any HIP call."""
+    d = wi.make_desc("bf16", 16, 8, 131072)
+    dd = wi.DecodeDesc(32, 147, 1884, 0.0, 0)
+    assert wi.decode_sizes(d, dd) > wi.NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced
+    bufs = wi.IndexBufs(*([0x100000] * 10))
+    rc = L.wi_decode_attention_noalloc(ctypes.byref(d), ctypes.byref(dd), ctypes.byref(bufs),
+                                       fake, fake, None, None, None, 0, None)
+    assert rc == 3
+    assert "static" in L.wi_last_error().decode()
+
+
+def test_noalloc_validates_like_the_workspace_entry_point(L):
+    d = wi.make_desc("bf16", 1, 8, 131072)
+    dd = wi.DecodeDesc(32, 147, 1884, 0.0, 0)
+    fake = ctypes.c_void_p(0x100000)
+    bufs = wi.IndexBufs(*([0x100000] * 10))
+    for q, out, code in [(None, fake, 1), (fake, None, 1), (ctypes.c_void_p(0x100004), fake, 1)]:
+        rc = L.wi_decode_attention_noalloc(ctypes.byref(d), ctypes.byref(dd), ctypes.byref(bufs),
+                                           q, out, None, None, None, 0, None)
+        assert rc == code
+    bad = wi.DecodeDesc(30, 147, 1884, 0.0, 0)  # 30 query heads over 8 KV heads
+    rc = L.wi_decode_attention_noalloc(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(bufs),
+                                       fake, fake, None, None, None, 0, None)
+    assert rc == 2
