@@ -734,36 +734,60 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
                             : (item < nT ? (Rblk[pos] << lgT) + (t - Rtok[pos]) : 0);
       }
       // (b) loads: keys in the MFMA layout, two value dims per lane of every
-      // token, the estimation clusters' value sums
+      // token, the estimation clusters' value sums. Tiles and groups of rows
+      // with no item issue no loads (ntw and new_ are uniform over the wave):
+      // most waves carry only one kind of item when a workgroup owns few.
       uint4 ka[NTILE][NKL];
 #pragma unroll
       for (int j = 0; j < NTILE; j++) {
-        const int item = t0 + 16 * j + r16;
-        const uint8_t* kp =
-            item < nT ? (item < nS ? sk8 : kb8) + (int64_t)rowj[j] * RB : dummy;
+        if (16 * j < ntw) {
+          const int item = t0 + 16 * j + r16;
+          const uint8_t* kp =
+              item < nT ? (item < nS ? sk8 : kb8) + (int64_t)rowj[j] * RB : dummy;
 #pragma unroll
-        for (int s = 0; s < NKL; s++) {
-          if constexpr (DT == WI_BF16)
-            ka[j][s] = *reinterpret_cast<const uint4*>(kp + (32 * s + 8 * kg) * 2);
-          else
-            ka[j][s] = *reinterpret_cast<const uint4*>(kp + (32 * kg + 4 * s) * 4);
+          for (int s = 0; s < NKL; s++) {
+            if constexpr (DT == WI_BF16)
+              ka[j][s] = *reinterpret_cast<const uint4*>(kp + (32 * s + 8 * kg) * 2);
+            else
+              ka[j][s] = *reinterpret_cast<const uint4*>(kp + (32 * kg + 4 * s) * 4);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < NKL; s++) ka[j][s] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
       uint2 vr[TB];  // bf16: .x holds dims 2 lane, 2 lane + 1; fp32: both words
 #pragma unroll
-      for (int t = 0; t < TB; t++) {
-        const int row = rdl(rowj[t / 16], t % 16);
-        const uint8_t* vpt = t < ntw ? (t0 + t < nS ? sv8 : vb8) + (int64_t)row * RB : dummy;
-        if constexpr (DT == WI_BF16)
-          vr[t].x = *reinterpret_cast<const uint32_t*>(vpt + 4 * lane);
-        else
-          vr[t] = *reinterpret_cast<const uint2*>(vpt + 8 * lane);
+      for (int t8 = 0; t8 < TB; t8 += 8) {
+        if (t8 < ntw) {
+#pragma unroll
+          for (int t = t8; t < t8 + 8; t++) {
+            const int row = rdl(rowj[t / 16], t % 16);
+            const uint8_t* vpt =
+                t < ntw ? (t0 + t < nS ? sv8 : vb8) + (int64_t)row * RB : dummy;
+            if constexpr (DT == WI_BF16)
+              vr[t].x = *reinterpret_cast<const uint32_t*>(vpt + 4 * lane);
+            else
+              vr[t] = *reinterpret_cast<const uint2*>(vpt + 8 * lane);
+          }
+        } else {
+#pragma unroll
+          for (int t = t8; t < t8 + 8; t++) vr[t] = make_uint2(0u, 0u);
+        }
       }
       float2 vs[EB];
 #pragma unroll
-      for (int e = 0; e < EB; e++) {
-        const int ide = e < new_ ? Eid[e0 + e] : 0;
-        vs[e] = *reinterpret_cast<const float2*>(a.vsum + (uC + ide) * D + 2 * lane);
+      for (int e4 = 0; e4 < EB; e4 += 4) {
+        if (e4 < new_) {
+#pragma unroll
+          for (int e = e4; e < e4 + 4; e++) {
+            const int ide = e < new_ ? Eid[e0 + e] : 0;
+            vs[e] = *reinterpret_cast<const float2*>(a.vsum + (uC + ide) * D + 2 * lane);
+          }
+        } else {
+#pragma unroll
+          for (int e = e4; e < e4 + 4; e++) vs[e] = make_float2(0.f, 0.f);
+        }
       }
       // estimation logits in the head-per-column layout: lane (r16, kg) holds
       // clusters e0 + 4 kg + jj, head r16
