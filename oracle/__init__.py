@@ -68,7 +68,8 @@ class Desc(ctypes.Structure):
                 ("n_ctx", ctypes.c_int64), ("seg_len", ctypes.c_int32),
                 ("clusters_per_seg", ctypes.c_int32), ("n_sink", ctypes.c_int32),
                 ("n_local", ctypes.c_int32), ("n_iters", ctypes.c_int32),
-                ("seed", ctypes.c_uint64), ("layer_id", ctypes.c_uint32)]
+                ("seed", ctypes.c_uint64), ("layer_id", ctypes.c_uint32),
+                ("n_pending", ctypes.c_int64)]
 
 
 class DDesc(ctypes.Structure):
@@ -96,8 +97,10 @@ def lib():
         _lib.wio_assign.argtypes = [P, i32, i32, P, i32, P]
         _lib.wio_update.argtypes = [P, i32, i32, P, i32, i32, P, P]
         _lib.wio_build.argtypes = [P] * 15
-        _lib.wio_decode.argtypes = [P] * 16 + [i64, P]
-        _lib.wio_attend_sets.argtypes = [P] * 11 + [P, i32, P, i32, P]
+        _lib.wio_decode.argtypes = [P] * 18 + [i64, P]
+        _lib.wio_attend_sets.argtypes = [P] * 13 + [P, i32, P, i32, P]
+        _lib.wio_append.argtypes = [P] * 7
+        _lib.wio_extend.argtypes = [P] * 23
         _lib.wio_num_threads.restype = ctypes.c_int
     return _lib
 
@@ -107,10 +110,11 @@ def _p(a):
 
 
 def make_desc(dtype, batch, n_kv_heads, n_ctx, seg_len=8192, clusters_per_seg=512,
-              n_sink=4, n_local=64, n_iters=10, seed=0, layer_id=0, head_dim=128):
+              n_sink=4, n_local=64, n_iters=10, seed=0, layer_id=0, head_dim=128,
+              n_pending=0):
     return Desc(F32 if dtype in ("f32", F32) else BF16, batch, n_kv_heads, head_dim,
                 n_ctx, seg_len, clusters_per_seg, n_sink, n_local, n_iters, seed,
-                layer_id)
+                layer_id, n_pending)
 
 
 def sizes(desc):
@@ -209,7 +213,8 @@ def decode(desc, n_q_heads, k_retrieve, k_estimate, idx, q, scale=0.0,
     d = desc.head_dim
     k_e = min(k_estimate, C - k_retrieve)
     if exec_cap is None:
-        exec_cap = desc.n_sink + desc.n_local + int(np.sort(idx["sizes"], axis=1)[:, ::-1][:, :k_retrieve].sum(axis=1).max(initial=0))
+        exec_cap = desc.n_sink + desc.n_local + desc.n_pending + int(
+            np.sort(idx["sizes"], axis=1)[:, ::-1][:, :k_retrieve].sum(axis=1).max(initial=0))
     q = np.ascontiguousarray(q, dtype=np.float32)
     res = dict(out=np.empty((desc.batch, n_q_heads, d), np.float64),
                sel=np.empty((U, k_retrieve + max(k_e, 0)), np.int32),
@@ -218,7 +223,7 @@ def decode(desc, n_q_heads, k_retrieve, k_estimate, idx, q, scale=0.0,
     dd = DDesc(n_q_heads, k_retrieve, k_estimate, scale)
     keep = [np.ascontiguousarray(idx[k]) for k in (
         "centroids", "sizes", "vsum", "block_off", "kblk", "vblk", "slot_token",
-        "steady_k", "steady_v")]
+        "steady_k", "steady_v")] + _pending(desc, idx)
     rc = lib().wio_decode(ctypes.byref(desc), ctypes.byref(dd), *[_p(a) for a in keep],
                           _p(q), _p(res["out"]), _p(res["sel"]), _p(res["exec_tokens"]),
                           _p(res["n_exec"]), exec_cap, _p(res["gkey"]))
@@ -237,11 +242,73 @@ def attend_sets(desc, n_q_heads, idx, q, R, E, scale=0.0):
     dd = DDesc(n_q_heads, R.shape[1], E.shape[1], scale)
     keep = [np.ascontiguousarray(idx[k]) for k in (
         "centroids", "sizes", "vsum", "block_off", "kblk", "vblk", "steady_k", "steady_v")]
+    keep += _pending(desc, idx)
     rc = lib().wio_attend_sets(ctypes.byref(desc), ctypes.byref(dd), *[_p(a) for a in keep],
                                _p(q), _p(R), R.shape[1], _p(E), E.shape[1], _p(out))
     if rc != 0:
         raise ValueError("oracle attend failed")
     return out
+
+
+def _pending(desc, idx):
+    """The pending rows [U, seg_len, d] (None when nothing is pending)."""
+    if desc.n_pending == 0:
+        return [None, None]
+    return [np.ascontiguousarray(idx["pend_k"], dtype=np.float32),
+            np.ascontiguousarray(idx["pend_v"], dtype=np.float32)]
+
+
+def append(desc, idx, k_new, v_new):
+    """One decode step's token per sequence (k_new, v_new [B, H, d]): slides
+    the local window of idx in place and moves the token leaving it to the
+    pending rows. Returns the descriptor of the grown index (n_ctx + 1,
+    n_pending + 1)."""
+    U = desc.batch * desc.n_kv_heads
+    d = desc.head_dim
+    for key in ("pend_k", "pend_v"):
+        if key not in idx:
+            idx[key] = np.zeros((U, desc.seg_len, d), np.float32)
+    for key in ("steady_k", "steady_v", "pend_k", "pend_v"):
+        idx[key] = np.ascontiguousarray(idx[key], dtype=np.float32)
+    k_new = np.ascontiguousarray(k_new, dtype=np.float32)
+    v_new = np.ascontiguousarray(v_new, dtype=np.float32)
+    rc = lib().wio_append(ctypes.byref(desc), _p(idx["steady_k"]), _p(idx["steady_v"]),
+                          _p(idx["pend_k"]), _p(idx["pend_v"]), _p(k_new), _p(v_new))
+    if rc != 0:
+        raise ValueError("oracle append failed (pending segment full?)")
+    nd = Desc.from_buffer_copy(desc)
+    nd.n_ctx += 1
+    nd.n_pending += 1
+    return nd
+
+
+def extend(desc, idx):
+    """Cluster the full pending segment and return (descriptor, index) of the
+    grown index (n_pending = 0)."""
+    nd = Desc.from_buffer_copy(desc)
+    nd.n_pending = 0
+    ns, C, cap, T = sizes(nd)
+    U = desc.batch * desc.n_kv_heads
+    d = desc.head_dim
+    n_idx = desc.n_ctx - desc.n_sink - desc.n_local
+    nst = desc.n_sink + desc.n_local
+    out = dict(
+        centroids=np.empty((U, C, d), np.float32), sizes=np.empty((U, C), np.int32),
+        vsum=np.empty((U, C, d), np.float32), block_off=np.empty((U, C + 1), np.int32),
+        kblk=np.empty((U, cap * T, d), np.float32), vblk=np.empty((U, cap * T, d), np.float32),
+        slot_token=np.empty((U, cap * T), np.int32),
+        steady_k=np.empty((U, nst, d), np.float32), steady_v=np.empty((U, nst, d), np.float32),
+        assign=np.empty((U, n_idx), np.int32))
+    ins = [np.ascontiguousarray(idx[k]) for k in (
+        "centroids", "sizes", "vsum", "block_off", "kblk", "vblk", "slot_token",
+        "steady_k", "steady_v", "assign")] + _pending(desc, idx)
+    rc = lib().wio_extend(ctypes.byref(desc), *[_p(a) for a in ins],
+                          *[_p(out[k]) for k in ("centroids", "sizes", "vsum", "block_off",
+                                                 "kblk", "vblk", "slot_token", "steady_k",
+                                                 "steady_v", "assign")])
+    if rc != 0:
+        raise ValueError("oracle extend failed (pending segment not full?)")
+    return nd, out
 
 
 def num_threads() -> int:

@@ -81,16 +81,17 @@ def full_attention(q, K, V, scale):
     return softmax_list(q, K, V, np.ones(K.shape[0]), scale)
 
 
-def tripartite(q, K, V, members, centroids, R, E, n_sink, n_local, scale):
+def tripartite(q, K, V, members, centroids, R, E, n_sink, n_local, scale, extra=()):
     """Explicit-list tripartite attention for one query head.
 
-    members[c]: token positions of cluster c. Steady tokens and every token of
-    the R clusters are listed as themselves; each non-empty E cluster is one
-    entry with key = centroid, value = mean member value, multiplicity n_c.
+    members[c]: token positions of cluster c. Steady tokens, the extra exact
+    positions (pending decode-time tokens) and every token of the R clusters
+    are listed as themselves; each non-empty E cluster is one entry with
+    key = centroid, value = mean member value, multiplicity n_c.
     """
     n = K.shape[0]
     steady = list(range(n_sink)) + list(range(n - n_local, n))
-    toks = steady + [int(t) for c in R for t in members[c]]
+    toks = steady + [int(t) for t in extra] + [int(t) for c in R for t in members[c]]
     keys = [K[toks]]
     vals = [V[toks]]
     mult = [np.ones(len(toks))]

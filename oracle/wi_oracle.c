@@ -40,14 +40,18 @@
  * Reading: steady tokens are not clustered (they are always attended
  * exactly, so clustering them too would count them twice). */
 
+/* Clustered tokens: the indexed range minus the pending tokens (decode-time
+ * tokens whose segment has not filled yet). */
+static int64_t idx_count(const wio_desc *d) {
+  return d->n_ctx - d->n_sink - d->n_local - d->n_pending;
+}
+
 static int64_t seg_count(const wio_desc *d) {
-  int64_t n_idx = d->n_ctx - d->n_sink - d->n_local;
-  return (n_idx + d->seg_len - 1) / d->seg_len;
+  return (idx_count(d) + d->seg_len - 1) / d->seg_len;
 }
 
 static int64_t seg_len_of(const wio_desc *d, int64_t s) {
-  int64_t n_idx = d->n_ctx - d->n_sink - d->n_local;
-  int64_t left = n_idx - s * d->seg_len;
+  int64_t left = idx_count(d) - s * d->seg_len;
   return left < d->seg_len ? left : d->seg_len;
 }
 
@@ -59,8 +63,9 @@ static int tokens_per_block(const wio_desc *d) {
 int wio_sizes(const wio_desc *d, int64_t *n_segments, int64_t *n_clusters,
               int64_t *block_cap, int32_t *tpb) {
   if (d->head_dim != 128 || d->seg_len < 1 || d->clusters_per_seg < 1 ||
-      d->n_sink < 0 || d->n_local < 0 ||
-      d->n_ctx < (int64_t)d->n_sink + d->n_local + 1)
+      d->n_sink < 0 || d->n_local < 0 || d->n_pending < 0 ||
+      d->n_pending > d->seg_len ||
+      d->n_ctx < (int64_t)d->n_sink + d->n_local + d->n_pending + 1)
     return -1;
   int64_t ns = seg_count(d), C = 0;
   for (int64_t s = 0; s < ns; s++) {
@@ -68,7 +73,7 @@ int wio_sizes(const wio_desc *d, int64_t *n_segments, int64_t *n_clusters,
     C += n < d->clusters_per_seg ? n : d->clusters_per_seg;
   }
   int T = tokens_per_block(d);
-  int64_t n_idx = d->n_ctx - d->n_sink - d->n_local;
+  int64_t n_idx = idx_count(d);
   if (n_segments) *n_segments = ns;
   if (n_clusters) *n_clusters = C;
   if (block_cap) *block_cap = (n_idx + C * (T - 1)) / T;
@@ -263,6 +268,7 @@ int wio_build(const wio_desc *d, const float *K, const float *V,
   int64_t ns, C, cap;
   int32_t T;
   if (wio_sizes(d, &ns, &C, &cap, &T) != 0) return -1;
+  if (d->n_pending != 0) return -1; /* an index is built with nothing pending */
   const int D = d->head_dim;
   const int64_t N = d->n_ctx;
   const int64_t n_idx = N - d->n_sink - d->n_local;
@@ -377,7 +383,11 @@ static int rank_cmp(const void *pa, const void *pb) {
 }
 
 /* Tripartite attention for one query head ([blog] 2.1 and 3.3; [news] 3):
- *   steady zone and retrieval-zone clusters are attended exactly;
+ *   the steady zone, the pending tokens (decode-time tokens that left the
+ *   local window and wait for their segment to fill; they are no longer
+ *   steady and not yet clustered, so the reading taken is that they are
+ *   attended exactly) and the retrieval-zone clusters' tokens are attended
+ *   exactly;
  *   each estimation-zone cluster c with n_c > 0 stands for n_c keys equal to
  *   its centroid: it adds n_c * exp(s_c) to the softmax denominator and
  *   exp(s_c) * VS_c (its value sum) to the numerator ([blog] 3.3 "centroid
@@ -390,12 +400,16 @@ static void attend_head(const wio_desc *d, double scale, const float *qh,
                         const float *vsum, const int32_t *block_off,
                         const float *kblk, const float *vblk,
                         const float *steady_k, const float *steady_v,
+                        const float *pend_k, const float *pend_v,
                         int64_t C, int64_t cap, int T, const int32_t *R,
                         int n_r, const int32_t *E, int n_e, double *o) {
   const int D = d->head_dim;
   const int nst = d->n_sink + d->n_local;
+  const int64_t np = d->n_pending;
   const float *sk = steady_k + (size_t)u * nst * D;
   const float *sv = steady_v + (size_t)u * nst * D;
+  const float *pk = np > 0 ? pend_k + (size_t)u * d->seg_len * D : NULL;
+  const float *pv = np > 0 ? pend_v + (size_t)u * d->seg_len * D : NULL;
   const float *kb = kblk + (size_t)u * cap * T * D;
   const float *vb = vblk + (size_t)u * cap * T * D;
   const int32_t *bo = block_off + (size_t)u * (C + 1);
@@ -404,6 +418,10 @@ static void attend_head(const wio_desc *d, double scale, const float *qh,
   double m = -INFINITY;
   for (int j = 0; j < nst; j++) {
     double z = dot64(qh, sk + (size_t)j * D, D) * scale;
+    if (z > m) m = z;
+  }
+  for (int64_t j = 0; j < np; j++) {
+    double z = dot64(qh, pk + (size_t)j * D, D) * scale;
     if (z > m) m = z;
   }
   for (int r = 0; r < n_r; r++) {
@@ -427,6 +445,11 @@ static void attend_head(const wio_desc *d, double scale, const float *qh,
     double p = exp(dot64(qh, sk + (size_t)j * D, D) * scale - m);
     den += p;
     for (int t = 0; t < D; t++) o[t] += p * (double)sv[(size_t)j * D + t];
+  }
+  for (int64_t j = 0; j < np; j++) {
+    double p = exp(dot64(qh, pk + (size_t)j * D, D) * scale - m);
+    den += p;
+    for (int t = 0; t < D; t++) o[t] += p * (double)pv[(size_t)j * D + t];
   }
   for (int r = 0; r < n_r; r++) {
     int32_t c = R[r];
@@ -453,7 +476,8 @@ int wio_decode(const wio_desc *d, const wio_ddesc *dd, const float *centroids,
                const int32_t *sizes, const float *vsum,
                const int32_t *block_off, const float *kblk, const float *vblk,
                const int32_t *slot_token, const float *steady_k,
-               const float *steady_v, const float *q, double *out,
+               const float *steady_v, const float *pend_k,
+               const float *pend_v, const float *q, double *out,
                int32_t *sel, int32_t *exec_tokens, int32_t *n_exec,
                int64_t exec_cap, double *gkey) {
   int64_t ns, C, cap;
@@ -496,8 +520,9 @@ int wio_decode(const wio_desc *d, const wio_ddesc *dd, const float *centroids,
     if (sel)
       for (int r = 0; r < K_r + K_e; r++) sel[(size_t)u * (K_r + K_e) + r] = rk[r].id;
     /* Execution buffer order ([blog] 3.2): steady tokens in position order,
-     * then each retrieved cluster's tokens (fragments skipped), clusters in
-     * rank order, tokens in ascending position. */
+     * then the pending tokens in position order, then each retrieved
+     * cluster's tokens (fragments skipped), clusters in rank order, tokens in
+     * ascending position. */
     if (exec_tokens || n_exec) {
       const int32_t *bo = block_off + (size_t)u * (C + 1);
       const int32_t *cnt = sizes + (size_t)u * C;
@@ -507,6 +532,9 @@ int wio_decode(const wio_desc *d, const wio_ddesc *dd, const float *centroids,
         int64_t tok = j < d->n_sink ? j : d->n_ctx - d->n_local + (j - d->n_sink);
         if (exec_tokens && pos < exec_cap) exec_tokens[(size_t)u * exec_cap + pos] = (int32_t)tok;
       }
+      const int64_t p0 = d->n_sink + idx_count(d); /* first pending position */
+      for (int64_t j = 0; j < d->n_pending; j++, pos++)
+        if (exec_tokens && pos < exec_cap) exec_tokens[(size_t)u * exec_cap + pos] = (int32_t)(p0 + j);
       for (int r = 0; r < K_r; r++) {
         int32_t c = R[r];
         for (int32_t j = 0; j < cnt[c]; j++, pos++)
@@ -517,8 +545,9 @@ int wio_decode(const wio_desc *d, const wio_ddesc *dd, const float *centroids,
     }
     for (int j = 0; j < G; j++)
       attend_head(d, scale, qg + (size_t)j * D, u, centroids, sizes, vsum,
-                  block_off, kblk, vblk, steady_k, steady_v, C, cap, T, R, K_r,
-                  E, K_e, out + ((size_t)b * dd->n_q_heads + (size_t)h * G + j) * D);
+                  block_off, kblk, vblk, steady_k, steady_v, pend_k, pend_v, C,
+                  cap, T, R, K_r, E, K_e,
+                  out + ((size_t)b * dd->n_q_heads + (size_t)h * G + j) * D);
     free(rk);
     free(R);
     free(E);
@@ -531,6 +560,7 @@ int wio_attend_sets(const wio_desc *d, const wio_ddesc *dd,
                     const float *vsum, const int32_t *block_off,
                     const float *kblk, const float *vblk,
                     const float *steady_k, const float *steady_v,
+                    const float *pend_k, const float *pend_v,
                     const float *q, const int32_t *R, int32_t n_r,
                     const int32_t *E, int32_t n_e, double *out) {
   int64_t ns, C, cap;
@@ -547,9 +577,148 @@ int wio_attend_sets(const wio_desc *d, const wio_ddesc *dd,
     const float *qg = q + ((size_t)b * dd->n_q_heads + (size_t)h * G) * D;
     for (int j = 0; j < G; j++)
       attend_head(d, scale, qg + (size_t)j * D, u, centroids, sizes, vsum,
-                  block_off, kblk, vblk, steady_k, steady_v, C, cap, T,
-                  R + (size_t)u * n_r, n_r, E + (size_t)u * n_e, n_e,
+                  block_off, kblk, vblk, steady_k, steady_v, pend_k, pend_v, C,
+                  cap, T, R + (size_t)u * n_r, n_r, E + (size_t)u * n_e, n_e,
                   out + ((size_t)b * dd->n_q_heads + (size_t)h * G + j) * D);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode steps that grow the index. Generating token t reads the history and
+ * then appends the current token's key and value ([blog] 1.1, read/write
+ * pattern; the cache is kept like a ring buffer). The steady zone is the
+ * first n_sink and the last n_local tokens ([blog] 2.1), so appending
+ * position n_ctx moves position n_ctx - n_local out of the local window.
+ * Reading: that token becomes pending -- attended exactly -- until seg_len
+ * such tokens form the next segment, which is then clustered like every
+ * segment ([blog] 2.1: k-means per 8K-token segment, segments independent). */
+int wio_append(const wio_desc *d, float *steady_k, float *steady_v,
+               float *pend_k, float *pend_v, const float *k_new,
+               const float *v_new) {
+  int64_t ns, C, cap;
+  int32_t T;
+  if (wio_sizes(d, &ns, &C, &cap, &T) != 0) return -1;
+  if (d->n_pending >= d->seg_len) return -1;
+  const int D = d->head_dim;
+  const int nst = d->n_sink + d->n_local;
+  const int64_t U = (int64_t)d->batch * d->n_kv_heads;
+  for (int64_t u = 0; u < U; u++) {
+    float *sk = steady_k + (size_t)u * nst * D, *sv = steady_v + (size_t)u * nst * D;
+    float *pk = pend_k + ((size_t)u * d->seg_len + d->n_pending) * D;
+    float *pv = pend_v + ((size_t)u * d->seg_len + d->n_pending) * D;
+    const float *kn = k_new + (size_t)u * D, *vn = v_new + (size_t)u * D;
+    if (d->n_local > 0) {
+      /* the oldest local token leaves the window */
+      memcpy(pk, sk + (size_t)d->n_sink * D, sizeof(float) * D);
+      memcpy(pv, sv + (size_t)d->n_sink * D, sizeof(float) * D);
+      memmove(sk + (size_t)d->n_sink * D, sk + (size_t)(d->n_sink + 1) * D,
+              sizeof(float) * (size_t)(d->n_local - 1) * D);
+      memmove(sv + (size_t)d->n_sink * D, sv + (size_t)(d->n_sink + 1) * D,
+              sizeof(float) * (size_t)(d->n_local - 1) * D);
+      memcpy(sk + (size_t)(nst - 1) * D, kn, sizeof(float) * D);
+      memcpy(sv + (size_t)(nst - 1) * D, vn, sizeof(float) * D);
+    } else {
+      memcpy(pk, kn, sizeof(float) * D);
+      memcpy(pv, vn, sizeof(float) * D);
+    }
+  }
+  return 0;
+}
+
+int wio_extend(const wio_desc *d, const float *centroids, const int32_t *sizes,
+               const float *vsum, const int32_t *block_off, const float *kblk,
+               const float *vblk, const int32_t *slot_token,
+               const float *steady_k, const float *steady_v,
+               const int32_t *assign, const float *pend_k, const float *pend_v,
+               float *n_centroids, int32_t *n_sizes, float *n_vsum,
+               int32_t *n_block_off, float *n_kblk, float *n_vblk,
+               int32_t *n_slot_token, float *n_steady_k, float *n_steady_v,
+               int32_t *n_assign) {
+  int64_t ns, C, cap, ns2, C2, cap2;
+  int32_t T, T2;
+  if (wio_sizes(d, &ns, &C, &cap, &T) != 0) return -1;
+  if (d->n_pending != d->seg_len) return -1;
+  wio_desc dn = *d;
+  dn.n_pending = 0;
+  if (wio_sizes(&dn, &ns2, &C2, &cap2, &T2) != 0) return -1;
+  const int D = d->head_dim;
+  const int n = d->seg_len;
+  const int k = n < d->clusters_per_seg ? n : d->clusters_per_seg;
+  if (C2 != C + k) return -1;
+  const int64_t n_idx = idx_count(d);
+  const int64_t p0 = d->n_sink + n_idx; /* first pending position */
+  const int64_t s_new = ns;             /* the new segment's ordinal */
+  const int nst = d->n_sink + d->n_local;
+  const int64_t U = (int64_t)d->batch * d->n_kv_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < U; u++) {
+    const int64_t b = u / d->n_kv_heads, h = u % d->n_kv_heads;
+    const float *X = pend_k + (size_t)u * n * D;
+    const float *Vp = pend_v + (size_t)u * n * D;
+    /* the new segment, clustered as wio_build clusters a segment */
+    float *Cn = n_centroids + ((size_t)u * C2 + C) * D;
+    int32_t *cnt = n_sizes + (size_t)u * C2 + C;
+    int32_t *picks = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    wio_kmeanspp(X, n, D, k, d->seed, (uint64_t)b, d->layer_id, (uint64_t)h,
+                 (uint64_t)s_new, picks);
+    for (int j = 0; j < k; j++)
+      memcpy(Cn + (size_t)j * D, X + (size_t)picks[j] * D, sizeof(float) * D);
+    free(picks);
+    int32_t *a = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+    const int iters = d->n_iters > 0 ? d->n_iters : 1;
+    for (int t = 0; t < iters; t++) {
+      wio_assign(X, n, D, Cn, k, a);
+      if (d->n_iters > 0) wio_update(X, n, D, a, k, d->dtype, Cn, cnt);
+    }
+    if (d->n_iters == 0) {
+      for (int c = 0; c < k; c++) cnt[c] = 0;
+      for (int i = 0; i < n; i++) cnt[a[i]]++;
+    }
+    /* the old clusters, blocks, steady rows and assignments, unchanged */
+    memcpy(n_centroids + (size_t)u * C2 * D, centroids + (size_t)u * C * D,
+           sizeof(float) * (size_t)C * D);
+    memcpy(n_sizes + (size_t)u * C2, sizes + (size_t)u * C, sizeof(int32_t) * (size_t)C);
+    memcpy(n_vsum + (size_t)u * C2 * D, vsum + (size_t)u * C * D, sizeof(float) * (size_t)C * D);
+    const int32_t *bo = block_off + (size_t)u * (C + 1);
+    int32_t *nbo = n_block_off + (size_t)u * (C2 + 1);
+    memcpy(nbo, bo, sizeof(int32_t) * (size_t)(C + 1));
+    const int64_t used = bo[C];
+    int32_t *nst_tok = n_slot_token + (size_t)u * cap2 * T;
+    float *nkb = n_kblk + (size_t)u * cap2 * T * D, *nvb = n_vblk + (size_t)u * cap2 * T * D;
+    for (int64_t j = 0; j < cap2 * T; j++) nst_tok[j] = -1;
+    memset(nkb, 0, sizeof(float) * (size_t)cap2 * T * D);
+    memset(nvb, 0, sizeof(float) * (size_t)cap2 * T * D);
+    memcpy(nst_tok, slot_token + (size_t)u * cap * T, sizeof(int32_t) * (size_t)used * T);
+    memcpy(nkb, kblk + (size_t)u * cap * T * D, sizeof(float) * (size_t)used * T * D);
+    memcpy(nvb, vblk + (size_t)u * cap * T * D, sizeof(float) * (size_t)used * T * D);
+    memcpy(n_steady_k + (size_t)u * nst * D, steady_k + (size_t)u * nst * D,
+           sizeof(float) * (size_t)nst * D);
+    memcpy(n_steady_v + (size_t)u * nst * D, steady_v + (size_t)u * nst * D,
+           sizeof(float) * (size_t)nst * D);
+    memcpy(n_assign + (size_t)u * (n_idx + n), assign + (size_t)u * n_idx,
+           sizeof(int32_t) * (size_t)n_idx);
+    /* the new clusters take the next ids and the blocks after the used ones;
+     * members in ascending position, value sums in float64 */
+    for (int c = 0; c < k; c++) nbo[C + c + 1] = nbo[C + c] + (cnt[c] + T - 1) / T;
+    if (nbo[C + k] > cap2) abort(); /* unreachable: cap2 bounds the used blocks */
+    int32_t *fill = (int32_t *)calloc((size_t)k, sizeof(int32_t));
+    double *vs = (double *)calloc((size_t)k * D, sizeof(double));
+    for (int i = 0; i < n; i++) {
+      const int c = a[i];
+      const int64_t slot = (int64_t)nbo[C + c] * T + fill[c]++;
+      nst_tok[slot] = (int32_t)(p0 + i);
+      memcpy(nkb + slot * D, X + (size_t)i * D, sizeof(float) * D);
+      memcpy(nvb + slot * D, Vp + (size_t)i * D, sizeof(float) * D);
+      for (int t = 0; t < D; t++) vs[(size_t)c * D + t] += (double)Vp[(size_t)i * D + t];
+      n_assign[(size_t)u * (n_idx + n) + n_idx + i] = (int32_t)(C + c);
+    }
+    for (int c = 0; c < k; c++)
+      for (int t = 0; t < D; t++)
+        n_vsum[((size_t)u * C2 + C + c) * D + t] = (float)vs[(size_t)c * D + t];
+    free(fill);
+    free(vs);
+    free(a);
   }
   return 0;
 }

@@ -32,6 +32,11 @@ typedef struct {
   int32_t seg_len, clusters_per_seg, n_sink, n_local, n_iters;
   uint64_t seed;
   uint32_t layer_id;
+  /* Tokens that have left the local window during decode and wait, attended
+   * exactly, for their segment to fill: positions [n_sink + n_idx, n_sink +
+   * n_idx + n_pending) with n_idx = n_ctx - n_sink - n_local - n_pending the
+   * clustered range. 0 for an index as built. */
+  int64_t n_pending;
 } wio_desc;
 
 typedef struct {
@@ -90,7 +95,8 @@ int wio_decode(const wio_desc *d, const wio_ddesc *dd, const float *centroids,
                const int32_t *sizes, const float *vsum,
                const int32_t *block_off, const float *kblk, const float *vblk,
                const int32_t *slot_token, const float *steady_k,
-               const float *steady_v, const float *q, double *out,
+               const float *steady_v, const float *pend_k,
+               const float *pend_v, const float *q, double *out,
                int32_t *sel, int32_t *exec_tokens, int32_t *n_exec,
                int64_t exec_cap, double *gkey);
 
@@ -102,8 +108,39 @@ int wio_attend_sets(const wio_desc *d, const wio_ddesc *dd,
                     const float *vsum, const int32_t *block_off,
                     const float *kblk, const float *vblk,
                     const float *steady_k, const float *steady_v,
+                    const float *pend_k, const float *pend_v,
                     const float *q, const int32_t *R, int32_t n_r,
                     const int32_t *E, int32_t n_e, double *out);
+
+/* ---- decode steps that grow the index -------------------------------- */
+/* One appended token per sequence: k_new, v_new [B][H][d]. The local window
+ * slides by one: the token leaving it (position n_ctx - n_local; the new
+ * token itself when n_local = 0) becomes pending row n_pending; the steady
+ * rows keep the sinks, then the local window in position order. steady_k/v
+ * [U][n_sink+n_local][d] and pend_k/v [U][seg_len][d] are updated in place;
+ * afterwards the index is described by n_ctx + 1 and n_pending + 1. Returns
+ * -1 when n_pending = seg_len already (the segment must be clustered first). */
+int wio_append(const wio_desc *d, float *steady_k, float *steady_v,
+               float *pend_k, float *pend_v, const float *k_new,
+               const float *v_new);
+
+/* Cluster a full pending segment (n_pending = seg_len) as the next segment of
+ * the stream and write the grown index: its geometry is that of d with
+ * n_pending = 0. The new segment is clustered exactly as the build clusters
+ * a segment (k-means++ from the random stream of (seed, b, layer, h,
+ * segment ordinal), then n_iters Lloyd iterations), its clusters take the
+ * next ids and its blocks follow the index's used blocks. Inputs are the
+ * index arrays for d (old geometry) and the pending rows; outputs the arrays
+ * for the new geometry (caller-allocated). */
+int wio_extend(const wio_desc *d, const float *centroids, const int32_t *sizes,
+               const float *vsum, const int32_t *block_off, const float *kblk,
+               const float *vblk, const int32_t *slot_token,
+               const float *steady_k, const float *steady_v,
+               const int32_t *assign, const float *pend_k, const float *pend_v,
+               float *n_centroids, int32_t *n_sizes, float *n_vsum,
+               int32_t *n_block_off, float *n_kblk, float *n_vblk,
+               int32_t *n_slot_token, float *n_steady_k, float *n_steady_v,
+               int32_t *n_assign);
 
 int wio_num_threads(void);
 
