@@ -65,10 +65,15 @@ enum { WI_F32 = 0, WI_BF16 = 1 };
 
 /* Index shape. One unit = (sequence b, KV head h) of one layer.
  * Steady zone: positions [0, n_sink) and [n_ctx - n_local, n_ctx).
- * Indexed tokens: [n_sink, n_ctx - n_local), cut into consecutive segments of
- * seg_len tokens (the last one may be short); segment s has
+ * Pending tokens (decode-time only, see wi_append_token): the n_pending
+ * positions just before the local window; they have left the window, wait for
+ * their segment to fill and are attended exactly.
+ * Clustered tokens: [n_sink, n_ctx - n_local - n_pending), n_idx of them, cut
+ * into consecutive segments of seg_len tokens (as built, the last one may be
+ * short; segments added by wi_extend_index are full); segment s has
  * C_s = min(clusters_per_seg, n_s) clusters; cluster ids are contiguous by
- * segment, so C = sum_s C_s clusters per unit.
+ * segment, so C = sum_s C_s clusters per unit (as if the n_idx clustered
+ * tokens were cut from the start, which gives the same count).
  * Tokens per 2 KB block: T = 2048 / (head_dim * bytes(dtype)) = 8 (bf16) or
  * 4 (fp32). */
 typedef struct {
@@ -87,11 +92,12 @@ typedef struct {
   int64_t kv_stride_b;      /* element strides of the K and V inputs         */
   int64_t kv_stride_h;      /*   [B, H, N, head_dim]; head_dim contiguous;   */
   int64_t kv_stride_t;      /*   all strides must be multiples of 8          */
+  int64_t n_pending;        /* 0 .. seg_len; 0 for wi_build_index            */
 } wi_index_desc;
 
 /* Index buffers (device memory, caller-owned). C and cap come from
- * wi_index_sizes; U = batch * n_kv_heads; n_idx = n_ctx - n_sink - n_local;
- * n_st = n_sink + n_local.
+ * wi_index_sizes; U = batch * n_kv_heads; n_idx = n_ctx - n_sink - n_local -
+ * n_pending; n_st = n_sink + n_local.
  *   centroids    [U][C][128] dtype   cluster means (rounded to dtype)
  *   cluster_size [U][C] int32        members per cluster
  *   value_sum    [U][C][128] float   sum of member values (fp64, rounded)
@@ -101,7 +107,10 @@ typedef struct {
  *   slot_token   [U][cap*T] int32    token position of each slot, -1 = pad
  *   steady_k     [U][n_st][128]      keys of the steady zone, in order
  *   steady_v     [U][n_st][128]      values of the steady zone
- *   assign       [U][n_idx] int32    cluster id of each indexed token
+ *   assign       [U][n_idx] int32    cluster id of each clustered token
+ *   pend_k       [U][seg_len][128]   pending keys in position order (decode-
+ *   pend_v       [U][seg_len][128]   time growth only; may be NULL while
+ *                                    n_pending = 0 and no token is appended)
  * Cluster c's members occupy slots [T*block_off[c], T*block_off[c] + size[c])
  * in ascending position; remaining slots of its last block, and all blocks
  * past block_off[C], hold token -1 and zero data. */
@@ -116,6 +125,8 @@ typedef struct {
   void *steady_k;
   void *steady_v;
   int32_t *assign;
+  void *pend_k;
+  void *pend_v;
 } wi_index_bufs;
 
 /* Host-only: sizes derived from the descriptor. Any output pointer may be
@@ -124,7 +135,7 @@ wi_status wi_index_sizes(const wi_index_desc *desc, int64_t *n_segments,
                          int64_t *n_clusters, int64_t *block_cap,
                          size_t *workspace_bytes);
 
-/* Build the index of every unit.
+/* Build the index of every unit (desc->n_pending must be 0).
  *   k, v          device [B][H][N][128] dtype, strides from desc
  *   init_centroids NULL: k-means++ seeding per segment (first centroid
  *                 uniform, then D^2 sampling; counter-based random stream
@@ -172,18 +183,20 @@ wi_status wi_decode_sizes(const wi_index_desc *desc,
  *   larger first, lower id on equal float32 keys.
  *   Ranks [0, K_r) form the retrieval zone R, the next
  *   min(K_e, C - K_r) ranks the estimation zone E. For each query head j:
- *     out_j = (sum_{i in steady + members(R)} e^{z_i} v_i
+ *     out_j = (sum_{i in steady + pending + members(R)} e^{z_i} v_i
  *              + sum_{c in E, n_c > 0} e^{s_c} VS_c)
  *           / (sum_{i} e^{z_i} + sum_{c in E, n_c > 0} n_c e^{s_c}),
  *   z_i = scale <q_j, k_i>, s_c = scale <q_j, centroid_c>.
  * Optional debug outputs (written only when non-NULL):
  *   sel_ids      device [U][K_r + K_e'] cluster ids in rank order
  *   exec_tokens  device [U][exec_cap] token positions of the execution
- *                buffer: steady positions in order, then each retrieved
- *                cluster's members (rank order, ascending position);
+ *                buffer: steady positions in order, then the pending
+ *                positions in order, then each retrieved cluster's members
+ *                (rank order, ascending position);
  *                entries past exec_cap are dropped; needs slot_token
  *   n_exec       device [U] execution-buffer length (may exceed exec_cap)
- *   bufs->assign is not read; bufs->slot_token only for exec_tokens. The
+ *   bufs->assign is not read; bufs->slot_token only for exec_tokens;
+ *   bufs->pend_k/pend_v only when n_pending > 0. The
  *   index must be one wi_build_index wrote (cluster c's members in the
  *   first cluster_size[c] slots from block block_off[c], within block_cap).
  *   NaN in q or the centroids leaves the selection unspecified (no fault).
@@ -197,6 +210,42 @@ wi_status wi_decode_attention(const wi_index_desc *desc,
                               int32_t *exec_tokens, int32_t *n_exec,
                               int64_t exec_cap, void *ws, size_t ws_bytes,
                               hipStream_t stream);
+
+/* Decode-time growth of the index (framerc blog section 1.1: generating a
+ * token reads the cached history and then appends the token's KV, the cache
+ * being kept like a ring buffer; section 2.1: the steady zone is the first
+ * n_sink and last n_local tokens, and clusters are formed per seg_len-token
+ * segment). One token per sequence is appended per call: the local window
+ * slides by one and the token leaving it (position n_ctx - n_local; the new
+ * token itself when n_local = 0) becomes pending row n_pending. Once
+ * seg_len tokens are pending, wi_extend_index clusters them as the next
+ * segment.
+ *   k_new, v_new  device [B][H][128] dtype, the new token's key and value
+ *   bufs          the index for desc; steady_k/v and pend_k/v are updated
+ *                 in place (pend_k/v required)
+ * Afterwards the index is described by n_ctx + 1 and n_pending + 1.
+ * Returns WI_E_INVALID when n_pending = seg_len (extend first). */
+wi_status wi_append_token(const wi_index_desc *desc, const wi_index_bufs *bufs,
+                          const void *k_new, const void *v_new,
+                          hipStream_t stream);
+
+/* Host-only: workspace bytes of wi_extend_index for desc (n_pending =
+ * seg_len). */
+wi_status wi_extend_sizes(const wi_index_desc *desc, size_t *workspace_bytes);
+
+/* Cluster the full pending segment (desc->n_pending = seg_len) as the
+ * stream's next segment and write the grown index to new_bufs, whose
+ * geometry is desc with n_pending = 0 (sizes from wi_index_sizes of that
+ * descriptor). The segment is clustered exactly as wi_build_index clusters a
+ * segment: k-means++ from the random stream keyed by (seed, b, layer_id, h,
+ * segment ordinal = the old index's segment count), then n_iters Lloyd
+ * iterations; its clusters take ids C .. C + C_s - 1 and its blocks follow
+ * the old index's used blocks. Every other cluster, block, steady row and
+ * assignment is copied unchanged. Old and new buffers must not overlap, except
+ * new_bufs->pend_k/v, which may alias the old ones (they are not written). */
+wi_status wi_extend_index(const wi_index_desc *desc, const wi_index_bufs *bufs,
+                          const wi_index_bufs *new_bufs, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 /* Largest decode workspace that wi_decode_attention_noalloc serves: 16 MiB
  * (the five model shapes of this library need at most 11.5 MiB: 8 units of

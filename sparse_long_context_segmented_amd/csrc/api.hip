@@ -47,11 +47,14 @@ wi_status make_geom(const wi_index_desc* d, wi::Geom* g) {
     return fail(WI_E_INVALID, "batch %d / n_kv_heads %d must be >= 1", d->batch, d->n_kv_heads);
   if (d->n_sink < 0 || d->n_local < 0)
     return fail(WI_E_INVALID, "n_sink %d / n_local %d must be >= 0", d->n_sink, d->n_local);
-  if (d->n_ctx < (int64_t)d->n_sink + d->n_local + 1)
-    return fail(WI_E_INVALID, "n_ctx %lld must be >= n_sink + n_local + 1", (long long)d->n_ctx);
   if (d->n_ctx >= (int64_t(1) << 31)) return fail(WI_E_INVALID, "n_ctx too large");
   if (d->seg_len < 1 || d->seg_len > wi::MAX_SEG)
     return fail(WI_E_INVALID, "seg_len %d outside [1, %d]", d->seg_len, wi::MAX_SEG);
+  if (d->n_pending < 0 || d->n_pending > d->seg_len)
+    return fail(WI_E_INVALID, "n_pending %lld outside [0, seg_len]", (long long)d->n_pending);
+  if (d->n_ctx < (int64_t)d->n_sink + d->n_local + d->n_pending + 1)
+    return fail(WI_E_INVALID, "n_ctx %lld must be >= n_sink + n_local + n_pending + 1",
+                (long long)d->n_ctx);
   if (d->clusters_per_seg < 1 || d->clusters_per_seg > wi::MAX_K)
     return fail(WI_E_INVALID, "clusters_per_seg %d outside [1, %d]", d->clusters_per_seg,
                 wi::MAX_K);
@@ -68,7 +71,9 @@ wi_status make_geom(const wi_index_desc* d, wi::Geom* g) {
   G.n_sink = d->n_sink;
   G.n_local = d->n_local;
   G.n_st = d->n_sink + d->n_local;
-  G.n_idx = d->n_ctx - G.n_st;
+  G.n_idx = d->n_ctx - G.n_st - d->n_pending;
+  G.n_pend = (int)d->n_pending;
+  G.seg_ord0 = 0;
   G.seg_len = d->seg_len;
   G.kk = d->clusters_per_seg;
   G.n_seg = (int)((G.n_idx + G.seg_len - 1) / G.seg_len);
@@ -189,6 +194,69 @@ int64_t carve_decode(const wi::Geom& g, const DecodeShape& ds, uint8_t* base, wi
     if (e_ != hipSuccess) return hip_fail(e_, where); \
   } while (0)
 
+// The build's launch sequence: k-means++ (or the given centroids), n_iters x
+// (assign, update), layout. k_blocks holds >= U * n_idx key rows (block_cap *
+// T >= n_idx) and is written only by the layout step, so k-means++ keeps its
+// chunked copy of the keys there until then.
+wi_status run_build(const wi::Geom& g, const void* k, const void* v, const void* init_centroids,
+                    const wi_index_bufs& b, wi::BuildWs& w, hipStream_t stream) {
+  w.kc = b.k_blocks;
+  if (init_centroids)
+    CHECK_HIP(wi::launch_copy_init(g, init_centroids, b.centroids, stream), "copy init");
+  else
+    CHECK_HIP(wi::launch_kpp(g, k, b.centroids, w, stream), "k-means++");
+  const int iters = g.n_iters > 0 ? g.n_iters : 1;
+  for (int t = 0; t < iters; t++) {
+    CHECK_HIP(wi::launch_assign(g, k, b.centroids, w, stream), "assign");
+    CHECK_HIP(wi::launch_sort_update(g, k, b.centroids, b.cluster_size, w, g.n_iters > 0,
+                                     stream),
+              "update");
+  }
+  CHECK_HIP(wi::launch_layout(g, k, v, b, w, stream), "layout");
+  return WI_OK;
+}
+
+// Geometry of the pending segment as a one-segment index of its own (no
+// steady zone; K/V rows are the pending rows [U][seg_len][128]), and the
+// carve of its buffers followed by its build workspace.
+wi_status segment_geom(const wi_index_desc* desc, const wi::Geom& g, wi::Geom* gs) {
+  wi_index_desc d = *desc;
+  d.n_ctx = g.seg_len;
+  d.n_sink = 0;
+  d.n_local = 0;
+  d.n_pending = 0;
+  d.kv_stride_b = (int64_t)g.H * g.seg_len * wi::D;
+  d.kv_stride_h = (int64_t)g.seg_len * wi::D;
+  d.kv_stride_t = wi::D;
+  wi_status st = make_geom(&d, gs);
+  if (st != WI_OK) return st;
+  gs->seg_ord0 = g.n_seg;  // the new segment's ordinal in the stream
+  return WI_OK;
+}
+
+int64_t carve_segment(const wi::Geom& gs, uint8_t* base, wi_index_bufs* b, wi::BuildWs* w) {
+  const int64_t e = gs.dtype == WI_BF16 ? 2 : 4;
+  const int64_t U = gs.U;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    uint8_t* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  wi_index_bufs t{};
+  t.centroids = take(U * gs.C * wi::D * e);
+  t.cluster_size = reinterpret_cast<int32_t*>(take(U * gs.C * 4));
+  t.value_sum = reinterpret_cast<float*>(take(U * gs.C * wi::D * 4));
+  t.block_off = reinterpret_cast<int32_t*>(take(U * (gs.C + 1) * 4));
+  t.k_blocks = take(U * gs.cap * gs.T * wi::D * e);
+  t.v_blocks = take(U * gs.cap * gs.T * wi::D * e);
+  t.slot_token = reinterpret_cast<int32_t*>(take(U * gs.cap * gs.T * 4));
+  t.assign = reinterpret_cast<int32_t*>(take(U * gs.n_idx * 4));
+  if (b) *b = t;
+  const int64_t wb = carve_build(gs, base ? base + off : nullptr, w);
+  return off + wb;
+}
+
 // Measurement hook state (per host thread).
 struct TimingRec {
   int id;
@@ -201,7 +269,8 @@ thread_local int t_cur = -1;
 
 const char* const kNames[wi::K_COUNT] = {
     "zero", "copy_init", "kpp_init", "kpp_weights", "kpp_round", "assign", "assign_fix",
-    "sort_update", "seg_scan", "layout", "score", "select_attend", "rank", "exec"};
+    "sort_update", "seg_scan", "layout", "score", "select_attend", "rank", "exec", "append",
+    "merge"};
 
 hipEvent_t take_event() {
   if (!t_pool.empty()) {
@@ -298,6 +367,7 @@ wi_status wi_build_index(const wi_index_desc* desc, const void* k, const void* v
   wi::Geom g;
   wi_status st = make_geom(desc, &g);
   if (st != WI_OK) return st;
+  if (g.n_pend != 0) return fail(WI_E_INVALID, "an index is built with n_pending = 0");
   CHECK_PTR(k, "k");
   CHECK_PTR(v, "v");
   if (init_centroids && !aligned16(init_centroids))
@@ -322,24 +392,9 @@ wi_status wi_build_index(const wi_index_desc* desc, const void* k, const void* v
   wi::BuildWs w;
   carve_build(g, reinterpret_cast<uint8_t*>(ws), &w);
 
-  // k_blocks holds >= U * n_idx key rows (block_cap * T >= n_idx) and is
-  // written only by the layout step, so k-means++ keeps its chunked copy of
-  // the keys there until then
-  w.kc = bufs->k_blocks;
-  if (init_centroids)
-    CHECK_HIP(wi::launch_copy_init(g, init_centroids, bufs->centroids, stream), "copy init");
-  else
-    CHECK_HIP(wi::launch_kpp(g, k, bufs->centroids, w, stream), "k-means++");
-  const int iters = g.n_iters > 0 ? g.n_iters : 1;
-  for (int t = 0; t < iters; t++) {
-    CHECK_HIP(wi::launch_assign(g, k, bufs->centroids, w, stream), "assign");
-    CHECK_HIP(wi::launch_sort_update(g, k, bufs->centroids, bufs->cluster_size, w,
-                                     g.n_iters > 0, stream),
-              "update");
-  }
-  CHECK_HIP(wi::launch_layout(g, k, v, *bufs, w, stream), "layout");
-  g_err[0] = 0;
-  return WI_OK;
+  st = run_build(g, k, v, init_centroids, *bufs, w, stream);
+  if (st == WI_OK) g_err[0] = 0;
+  return st;
 }
 
 wi_status wi_decode_sizes(const wi_index_desc* desc, const wi_decode_desc* ddesc,
@@ -380,6 +435,10 @@ wi_status validate_decode(const wi_index_desc* desc, const wi_decode_desc* ddesc
   if (g->n_st > 0) {
     CHECK_PTR(bufs->steady_k, "bufs->steady_k");
     CHECK_PTR(bufs->steady_v, "bufs->steady_v");
+  }
+  if (g->n_pend > 0) {
+    CHECK_PTR(bufs->pend_k, "bufs->pend_k");
+    CHECK_PTR(bufs->pend_v, "bufs->pend_v");
   }
   CHECK_PTR(q, "q");
   CHECK_PTR(out, "out");
@@ -475,6 +534,87 @@ wi_status wi_decode_attention_noalloc(const wi_index_desc* desc, const wi_decode
   st = scratch_for_current_device(&ws);
   if (st != WI_OK) return st;
   return run_decode(g, ds, bufs, q, out, sel_ids, exec_tokens, n_exec, exec_cap, ws, stream);
+}
+
+wi_status wi_append_token(const wi_index_desc* desc, const wi_index_bufs* bufs,
+                          const void* k_new, const void* v_new, hipStream_t stream) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  if (g.n_pend >= g.seg_len)
+    return fail(WI_E_INVALID, "n_pending = seg_len: cluster the segment (wi_extend_index) first");
+  if (!bufs) return fail(WI_E_INVALID, "bufs is NULL");
+  if (g.n_st > 0) {
+    CHECK_PTR(bufs->steady_k, "bufs->steady_k");
+    CHECK_PTR(bufs->steady_v, "bufs->steady_v");
+  }
+  CHECK_PTR(bufs->pend_k, "bufs->pend_k");
+  CHECK_PTR(bufs->pend_v, "bufs->pend_v");
+  CHECK_PTR(k_new, "k_new");
+  CHECK_PTR(v_new, "v_new");
+  CHECK_HIP(wi::launch_append(g, *bufs, k_new, v_new, stream), "append");
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_extend_sizes(const wi_index_desc* desc, size_t* workspace_bytes) {
+  wi::Geom g, gs;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  if (g.n_pend != g.seg_len)
+    return fail(WI_E_INVALID, "n_pending %d != seg_len %d", g.n_pend, g.seg_len);
+  st = segment_geom(desc, g, &gs);
+  if (st != WI_OK) return st;
+  if (workspace_bytes) *workspace_bytes = (size_t)carve_segment(gs, nullptr, nullptr, nullptr);
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_extend_index(const wi_index_desc* desc, const wi_index_bufs* bufs,
+                          const wi_index_bufs* new_bufs, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  wi::Geom g, gn, gs;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  if (g.n_pend != g.seg_len)
+    return fail(WI_E_INVALID, "n_pending %d != seg_len %d", g.n_pend, g.seg_len);
+  wi_index_desc dn = *desc;
+  dn.n_pending = 0;
+  st = make_geom(&dn, &gn);
+  if (st != WI_OK) return st;
+  st = segment_geom(desc, g, &gs);
+  if (st != WI_OK) return st;
+  if (gn.C != g.C + gs.C) return fail(WI_E_INVALID, "inconsistent cluster counts");
+  if (!bufs || !new_bufs) return fail(WI_E_INVALID, "bufs is NULL");
+  const wi_index_bufs* sides[2] = {bufs, new_bufs};
+  for (const wi_index_bufs* b : sides) {
+    CHECK_PTR(b->centroids, "centroids");
+    CHECK_PTR(b->cluster_size, "cluster_size");
+    CHECK_PTR(b->value_sum, "value_sum");
+    CHECK_PTR(b->block_off, "block_off");
+    CHECK_PTR(b->k_blocks, "k_blocks");
+    CHECK_PTR(b->v_blocks, "v_blocks");
+    CHECK_PTR(b->slot_token, "slot_token");
+    CHECK_PTR(b->assign, "assign");
+    if (g.n_st > 0) {
+      CHECK_PTR(b->steady_k, "steady_k");
+      CHECK_PTR(b->steady_v, "steady_v");
+    }
+  }
+  CHECK_PTR(bufs->pend_k, "bufs->pend_k");
+  CHECK_PTR(bufs->pend_v, "bufs->pend_v");
+  const int64_t need = carve_segment(gs, nullptr, nullptr, nullptr);
+  if (!ws || (int64_t)ws_bytes < need)
+    return fail(WI_E_WORKSPACE, "workspace %zu bytes < %lld required", ws_bytes, (long long)need);
+  if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
+  wi_index_bufs sb;
+  wi::BuildWs w;
+  carve_segment(gs, reinterpret_cast<uint8_t*>(ws), &sb, &w);
+  st = run_build(gs, bufs->pend_k, bufs->pend_v, nullptr, sb, w, stream);
+  if (st != WI_OK) return st;
+  CHECK_HIP(wi::launch_extend_merge(g, gn, gs, *bufs, sb, *new_bufs, stream), "merge");
+  g_err[0] = 0;
+  return WI_OK;
 }
 
 }  // extern "C"

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(NT) void kpp_init_kernel(Geom g, const void* __rest
   const int b = u / g.H, h = u % g.H;
   __shared__ float mu[D];
   __shared__ float red[4];
-  const int i0 = (int)scale53(draw_key(g.seed, b, g.layer, h, s, 0), (uint64_t)n);
+  const int i0 = (int)scale53(draw_key(g.seed, b, g.layer, h, s + g.seg_ord0, 0), (uint64_t)n);
   const int64_t first = seg_first(g, s);
   const void* r0 = krow<DT>(K, g, u, first + i0);
   load_mu<DT>(r0, mu);
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(NT, DT == WI_BF16 ? 8 : 5) void kpp_round_kernel(Ge
         q_s = -1;
       }
     } else {
-      const unsigned long long t = scale53(draw_key(g.seed, b, g.layer, h, s, r), W);
+      const unsigned long long t = scale53(draw_key(g.seed, b, g.layer, h, s + g.seg_ord0, r), W);
       const bool hit = lane < ns && incl > t && (incl - v) <= t;
       if (hit) {
         q_s = lane;

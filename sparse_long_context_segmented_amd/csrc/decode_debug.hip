@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void exec_kernel(
     const int32_t* __restrict__ ranked, const int32_t* __restrict__ sizes,
     const int32_t* __restrict__ block_off, const int32_t* __restrict__ slot_token,
     int C, int64_t capT, int T, int K_r, int M, int n_sink, int n_local, int64_t N,
-    int32_t* __restrict__ exec, int32_t* __restrict__ n_exec, int64_t exec_cap) {
+    int n_pend, int32_t* __restrict__ exec, int32_t* __restrict__ n_exec, int64_t exec_cap) {
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_st = n_sink + n_local;
@@ -41,10 +41,14 @@ __global__ __launch_bounds__(256) void exec_kernel(
   const int32_t* st = slot_token + (int64_t)u * capT;
   __shared__ int wsum[4];
   __shared__ int run_s;
-  if (tid == 0) run_s = n_st;
+  if (tid == 0) run_s = n_st + n_pend;
   if (exec) {
-    for (int j = tid; j < n_st && j < exec_cap; j += 256)
-      exec[(int64_t)u * exec_cap + j] = j < n_sink ? j : (int32_t)(N - n_local + (j - n_sink));
+    // steady positions, then the pending ones (just before the local window)
+    const int64_t p0 = N - n_local - n_pend;
+    for (int j = tid; j < n_st + n_pend && j < exec_cap; j += 256)
+      exec[(int64_t)u * exec_cap + j] =
+          j < n_sink ? j
+                     : (j < n_st ? (int32_t)(N - n_local + (j - n_sink)) : (int32_t)(p0 + j - n_st));
   }
   __syncthreads();
   for (int base = 0; base < K_r; base += 256) {
@@ -94,7 +98,7 @@ hipError_t launch_debug_outputs(const DecodeArgs& a, const wi_index_bufs& b,
   if (exec_tokens || n_exec) {
     WI_LAUNCH(K_EXEC, exec_kernel, dim3(g.U), dim3(256), 0, s, ranked, b.cluster_size,
                        b.block_off, b.slot_token, g.C, g.cap * g.T, g.T, a.K_r, M,
-                       g.n_sink, g.n_local, g.N, exec_tokens, n_exec, exec_cap);
+                       g.n_sink, g.n_local, g.N, g.n_pend, exec_tokens, n_exec, exec_cap);
   }
   return hipGetLastError();
 }

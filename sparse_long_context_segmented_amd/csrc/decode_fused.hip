@@ -10,7 +10,10 @@
 // Grid: W workgroups of 512 threads per unit (sequence, KV head). Cluster ids
 // are cut into groups of 16 consecutive ids; workgroup w owns the groups
 // w, w + W, w + 2W, ... (so every segment's clusters spread over all
-// workgroups of the unit) and the steady tokens [w n_st / W, (w+1) n_st / W).
+// workgroups of the unit) and the exactly attended rows outside the retrieved
+// clusters -- the n_st steady rows, then the n_pend pending rows (decode-time
+// tokens that left the local window and wait for their segment) -- [w n_x /
+// W, (w+1) n_x / W), n_x = n_st + n_pend.
 // At batch 1 a decode step moves a few tens of MB, so the kernel is bound by
 // latencies -- dependent memory round trips, LDS round trips, instruction
 // chains -- and is laid out to keep those few:
@@ -91,7 +94,9 @@ struct FusedArgs {
   float* part;             // [U][W][G][PART]
   int* tix;                // [U] arrival counters, zero on entry
   uint8_t* zone;           // nullable: [U][C] 1 = retrieval, 2 = estimation
-  int C, Cp, n_st, G, H, Hq, K_r, K_e, W, lgT, NB;
+  const void* pk;          // nullable while n_pend = 0: [U][seg_len] pending rows
+  const void* pv;
+  int C, Cp, n_st, n_pend, seg_len, G, H, Hq, K_r, K_e, W, lgT, NB;
   int64_t capT;
   float scale;
 };
@@ -263,7 +268,8 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   const int NP = BIG ? (C + CL - 1) / CL : 1;  // LDS passes over the keys
   const uint32_t* keyg = a.key + (int64_t)u * a.Cp;  // 16-byte aligned rows
   const int64_t uC = (int64_t)u * C;
-  const int s_lo = (int)((int64_t)a.n_st * w / W), s_hi = (int)((int64_t)a.n_st * (w + 1) / W);
+  const int n_x = a.n_st + a.n_pend;  // steady rows, then pending rows
+  const int s_lo = (int)((int64_t)n_x * w / W), s_hi = (int)((int64_t)n_x * (w + 1) / W);
   // own groups w, w + W, ... of the ng groups; own index k -> cluster id
   const int ng = (C + GRP - 1) / GRP;
   const int n_own = ng > w ? ((ng - 1 - w) / W + 1) * GRP : 0;
@@ -443,6 +449,15 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(a.vblk) + (int64_t)u * a.capT * RB;
   const uint8_t* sk8 = reinterpret_cast<const uint8_t*>(a.stk) + (int64_t)u * a.n_st * RB;
   const uint8_t* sv8 = reinterpret_cast<const uint8_t*>(a.stv) + (int64_t)u * a.n_st * RB;
+  // row x of the steady-then-pending rows (x < n_st + n_pend)
+  const uint8_t* pk8 = a.n_pend > 0 ? reinterpret_cast<const uint8_t*>(a.pk) +
+                                          (int64_t)u * a.seg_len * RB : sk8;
+  const uint8_t* pv8 = a.n_pend > 0 ? reinterpret_cast<const uint8_t*>(a.pv) +
+                                          (int64_t)u * a.seg_len * RB : sv8;
+  const int n_st = a.n_st;
+  auto xrow = [&](const uint8_t* st8, const uint8_t* p8, int x) {
+    return x < n_st ? st8 + (int64_t)x * RB : p8 + (int64_t)(x - n_st) * RB;
+  };
   // a valid row of at least RB bytes, read by lanes without an item
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.vsum + uC * D);
   const int lgT = a.lgT;
@@ -478,7 +493,8 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     // the steady rows of this workgroup (wave 0)
     if (wv == 0) {
       const int off = (lane & 31) * 128;
-      if (off < (s_hi - s_lo) * RB)
+      const int s_end = min(s_hi, n_st);  // the steady rows of the share
+      if (s_lo < s_end && off < (s_end - s_lo) * RB)
         wst = *reinterpret_cast<const uint32_t*>((lane < 32 ? sk8 : sv8) +
                                                    (int64_t)s_lo * RB + off);
     }
@@ -743,7 +759,8 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
         if (16 * j < ntw) {
           const int item = t0 + 16 * j + r16;
           const uint8_t* kp =
-              item < nT ? (item < nS ? sk8 : kb8) + (int64_t)rowj[j] * RB : dummy;
+              item < nT ? (item < nS ? xrow(sk8, pk8, rowj[j]) : kb8 + (int64_t)rowj[j] * RB)
+                        : dummy;
 #pragma unroll
           for (int s = 0; s < NKL; s++) {
             if constexpr (DT == WI_BF16)
@@ -764,7 +781,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
           for (int t = t8; t < t8 + 8; t++) {
             const int row = rdl(rowj[t / 16], t % 16);
             const uint8_t* vpt =
-                t < ntw ? (t0 + t < nS ? sv8 : vb8) + (int64_t)row * RB : dummy;
+                t < ntw ? (t0 + t < nS ? xrow(sv8, pv8, row) : vb8 + (int64_t)row * RB) : dummy;
             if constexpr (DT == WI_BF16)
               vr[t].x = *reinterpret_cast<const uint32_t*>(vpt + 4 * lane);
             else
@@ -1080,6 +1097,10 @@ hipError_t launch_fused(const DecodeArgs& da, const wi_index_bufs& bf, const voi
   fa.C = g.C;
   fa.Cp = (g.C + 3) & ~3;
   fa.n_st = g.n_st;
+  fa.n_pend = g.n_pend;
+  fa.seg_len = g.seg_len;
+  fa.pk = bf.pend_k;
+  fa.pv = bf.pend_v;
   fa.G = da.G;
   fa.H = g.H;
   fa.Hq = da.Hq;

@@ -32,6 +32,8 @@ struct Geom {
   uint32_t layer;
   int n_iters;
   int cmax;         // max clusters of any segment = min(kk, seg_len, n_idx)
+  int n_pend;       // pending tokens, positions [n_sink + n_idx, + n_pend)
+  int seg_ord0;     // ordinal of segment 0 in the k-means++ random stream
 };
 
 // Segment s of a unit: first indexed position, length, cluster count/base.
@@ -189,7 +191,7 @@ __device__ __forceinline__ float wave_max(float v) {
 enum KernelId {
   K_ZERO, K_COPY, K_KPP_INIT, K_KPP_WEIGHTS, K_KPP_ROUND, K_ASSIGN, K_ASSIGN_FIX,
   K_SORT_UPDATE, K_SEG_SCAN, K_LAYOUT, K_SCORE, K_FUSED, K_RANK,
-  K_EXEC, K_COUNT
+  K_EXEC, K_APPEND, K_MERGE, K_COUNT
 };
 void tmark_begin(KernelId id, hipStream_t s);
 void tmark_end(hipStream_t s);
@@ -231,6 +233,13 @@ hipError_t launch_score(const DecodeArgs& a, const void* centroids, const void* 
                         const DecodeWs& ws, hipStream_t s);
 hipError_t launch_fused(const DecodeArgs& a, const wi_index_bufs& b, const void* q,
                         float* out, const DecodeWs& ws, bool want_lists, hipStream_t s);
+hipError_t launch_append(const Geom& g, const wi_index_bufs& b, const void* k_new,
+                         const void* v_new, hipStream_t s);
+// The grown index nw (geometry gn) from the old index o (geometry go) and the
+// new segment sg clustered as a one-segment index (geometry gs).
+hipError_t launch_extend_merge(const Geom& go, const Geom& gn, const Geom& gs,
+                               const wi_index_bufs& o, const wi_index_bufs& sg,
+                               const wi_index_bufs& nw, hipStream_t s);
 hipError_t launch_debug_outputs(const DecodeArgs& a, const wi_index_bufs& b,
                                 const DecodeWs& ws, int32_t* sel_ids,
                                 int32_t* exec_tokens, int32_t* n_exec,

@@ -20,7 +20,8 @@ WI_F32, WI_BF16 = 0, 1
 STATUS = {0: "WI_OK", 1: "WI_E_INVALID", 2: "WI_E_UNSUPPORTED", 3: "WI_E_WORKSPACE",
           4: "WI_E_HIP"}
 EXPORTS = ("wi_index_sizes", "wi_build_index", "wi_decode_sizes", "wi_decode_attention",
-           "wi_decode_attention_noalloc", "wi_status_str", "wi_last_error",
+           "wi_decode_attention_noalloc", "wi_append_token", "wi_extend_sizes",
+           "wi_extend_index", "wi_status_str", "wi_last_error",
            "wi_timing_start", "wi_timing_stop", "wi_kernel_name")
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -39,13 +40,13 @@ class IndexDesc(ctypes.Structure):
                 ("n_local", ctypes.c_int32), ("n_iters", ctypes.c_int32),
                 ("seed", ctypes.c_uint64), ("layer_id", ctypes.c_uint32),
                 ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
-                ("kv_stride_t", ctypes.c_int64)]
+                ("kv_stride_t", ctypes.c_int64), ("n_pending", ctypes.c_int64)]
 
 
 class IndexBufs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "centroids", "cluster_size", "value_sum", "block_off", "k_blocks", "v_blocks",
-        "slot_token", "steady_k", "steady_v", "assign")]
+        "slot_token", "steady_k", "steady_v", "assign", "pend_k", "pend_v")]
 
 
 class DecodeDesc(ctypes.Structure):
@@ -77,6 +78,12 @@ def lib():
         L.wi_decode_attention.restype = ctypes.c_int
         L.wi_decode_attention_noalloc.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int64, P]
         L.wi_decode_attention_noalloc.restype = ctypes.c_int
+        L.wi_append_token.argtypes = [P, P, P, P, P]
+        L.wi_append_token.restype = ctypes.c_int
+        L.wi_extend_sizes.argtypes = [P, P]
+        L.wi_extend_sizes.restype = ctypes.c_int
+        L.wi_extend_index.argtypes = [P, P, P, P, ctypes.c_size_t, P]
+        L.wi_extend_index.restype = ctypes.c_int
         L.wi_status_str.argtypes = [ctypes.c_int]
         L.wi_status_str.restype = ctypes.c_char_p
         L.wi_last_error.argtypes = []
@@ -144,33 +151,45 @@ class Index:
     steady_k: torch.Tensor
     steady_v: torch.Tensor
     assign: torch.Tensor
+    pend_k: torch.Tensor | None = None   # [U, seg_len, 128]: pending rows (decode-time growth)
+    pend_v: torch.Tensor | None = None
 
     def bufs(self) -> IndexBufs:
         return IndexBufs(*[_ptr(getattr(self, n)) for n, _ in IndexBufs._fields_])
 
 
-def alloc_index(desc: IndexDesc, device="cuda") -> Index:
+def alloc_index(desc: IndexDesc, device="cuda", pending=None) -> Index:
+    """Buffers of an index for desc; pending: (pend_k, pend_v) to reuse, True
+    to allocate new pending rows, None for none."""
     ns, C, cap, _ = index_sizes(desc)
     U = desc.batch * desc.n_kv_heads
     T = 2048 // (128 * (4 if desc.dtype == WI_F32 else 2))
     dt = torch_dtype(desc)
-    n_idx = desc.n_ctx - desc.n_sink - desc.n_local
+    n_idx = desc.n_ctx - desc.n_sink - desc.n_local - desc.n_pending
     n_st = desc.n_sink + desc.n_local
     e = lambda *s, dtype=dt: torch.empty(*s, dtype=dtype, device=device)  # noqa: E731
+    pk = pv = None
+    if pending is True:
+        pk, pv = e(U, desc.seg_len, 128), e(U, desc.seg_len, 128)
+    elif pending is not None:
+        pk, pv = pending
     return Index(desc, e(U, C, 128), e(U, C, dtype=torch.int32), e(U, C, 128, dtype=torch.float32),
                  e(U, C + 1, dtype=torch.int32), e(U, cap * T, 128), e(U, cap * T, 128),
                  e(U, cap * T, dtype=torch.int32), e(U, max(n_st, 1), 128),
-                 e(U, max(n_st, 1), 128), e(U, n_idx, dtype=torch.int32))
+                 e(U, max(n_st, 1), 128), e(U, n_idx, dtype=torch.int32), pk, pv)
 
 
 def index_from_host(desc: IndexDesc, arrays: dict, device="cuda") -> Index:
     """Upload an index given as host arrays (keys as in the oracle's output)."""
     dt = torch_dtype(desc)
     t = lambda a, dtype=dt: torch.as_tensor(a).to(device=device, dtype=dtype).contiguous()  # noqa: E731
+    pk = t(arrays["pend_k"]) if "pend_k" in arrays else None
+    pv = t(arrays["pend_v"]) if "pend_v" in arrays else None
     return Index(desc, t(arrays["centroids"]), t(arrays["sizes"], torch.int32),
                  t(arrays["vsum"], torch.float32), t(arrays["block_off"], torch.int32),
                  t(arrays["kblk"]), t(arrays["vblk"]), t(arrays["slot_token"], torch.int32),
-                 t(arrays["steady_k"]), t(arrays["steady_v"]), t(arrays["assign"], torch.int32))
+                 t(arrays["steady_k"]), t(arrays["steady_v"]), t(arrays["assign"], torch.int32),
+                 pk, pv)
 
 
 def build_index(desc: IndexDesc, k: torch.Tensor, v: torch.Tensor,
@@ -227,6 +246,55 @@ def decode_attention_noalloc(index: Index, ddesc: DecodeDesc, q: torch.Tensor, o
         ctypes.byref(index.desc), ctypes.byref(ddesc), ctypes.byref(bufs), _ptr(q), _ptr(out),
         _ptr(sel_ids), _ptr(exec_tokens), _ptr(n_exec), exec_cap, _stream(stream)))
     return out
+
+
+def _copy_desc(desc: IndexDesc) -> IndexDesc:
+    return IndexDesc.from_buffer_copy(desc)
+
+
+def append_token(index: Index, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> Index:
+    """Run wi_append_token (k_new, v_new [B, H, 128]): slides the local window
+    of index in place and pends the departing token. Returns the same buffers
+    under the grown descriptor (n_ctx + 1, n_pending + 1); pending rows are
+    allocated on first use."""
+    desc = index.desc
+    U = desc.batch * desc.n_kv_heads
+    if index.pend_k is None:
+        dt = torch_dtype(desc)
+        index.pend_k = torch.empty(U, desc.seg_len, 128, dtype=dt, device=k_new.device)
+        index.pend_v = torch.empty(U, desc.seg_len, 128, dtype=dt, device=k_new.device)
+    bufs = index.bufs()
+    _check(lib().wi_append_token(ctypes.byref(desc), ctypes.byref(bufs), _ptr(k_new), _ptr(v_new),
+                                 _stream(stream)))
+    nd = _copy_desc(desc)
+    nd.n_ctx += 1
+    nd.n_pending += 1
+    index.desc = nd
+    return index
+
+
+def extend_sizes(desc: IndexDesc) -> int:
+    ws = ctypes.c_size_t()
+    _check(lib().wi_extend_sizes(ctypes.byref(desc), ctypes.byref(ws)))
+    return ws.value
+
+
+def extend_index(index: Index, ws: torch.Tensor | None = None, new: Index | None = None,
+                 stream=None) -> Index:
+    """Run wi_extend_index on an index whose pending segment is full: returns
+    the grown index (n_pending = 0; it keeps the pending buffers)."""
+    desc = index.desc
+    nd = _copy_desc(desc)
+    nd.n_pending = 0
+    if new is None:
+        new = alloc_index(nd, index.centroids.device, pending=(index.pend_k, index.pend_v))
+    wsb = extend_sizes(desc)
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=index.centroids.device)
+    ob, nb = index.bufs(), new.bufs()
+    _check(lib().wi_extend_index(ctypes.byref(desc), ctypes.byref(ob), ctypes.byref(nb),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return new
 
 
 def timing_start():

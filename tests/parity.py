@@ -68,12 +68,16 @@ def check_selection(sel_gpu: np.ndarray, gkey: np.ndarray, k_r: int) -> int:
 
 
 def exec_reference(idx: dict, sel: np.ndarray, k_r: int, n_ctx: int, T: int, n_sink=4,
-                   n_local=64):
-    """Execution-buffer tokens implied by a selection and an index."""
+                   n_local=64, n_pending=0):
+    """Execution-buffer tokens implied by a selection and an index: steady
+    positions, pending positions (just before the local window), then the
+    retrieved clusters' members in rank order."""
     res = []
+    p0 = n_ctx - n_local - n_pending
     for u in range(sel.shape[0]):
         bo, sz, st = idx["block_off"][u], idx["sizes"][u], idx["slot_token"][u]
         toks = list(range(n_sink)) + list(range(n_ctx - n_local, n_ctx))
+        toks += list(range(p0, p0 + n_pending))
         for c in sel[u][:k_r]:
             toks.extend(st[bo[c] * T: bo[c] * T + sz[c]].tolist())
         res.append(toks)
@@ -84,11 +88,15 @@ def index_to_host(ix: wi.Index, units=None) -> dict:
     """Index arrays on the host, [U, ...]; with units, only those units (in
     the order given)."""
     pick = (lambda t: t) if units is None else (lambda t: t[list(units)])  # noqa: E731
-    return dict(centroids=to_np(pick(ix.centroids)), sizes=to_np(pick(ix.cluster_size)),
-                vsum=to_np(pick(ix.value_sum)), block_off=to_np(pick(ix.block_off)),
-                kblk=to_np(pick(ix.k_blocks)), vblk=to_np(pick(ix.v_blocks)),
-                slot_token=to_np(pick(ix.slot_token)), steady_k=to_np(pick(ix.steady_k)),
-                steady_v=to_np(pick(ix.steady_v)), assign=to_np(pick(ix.assign)))
+    out = dict(centroids=to_np(pick(ix.centroids)), sizes=to_np(pick(ix.cluster_size)),
+               vsum=to_np(pick(ix.value_sum)), block_off=to_np(pick(ix.block_off)),
+               kblk=to_np(pick(ix.k_blocks)), vblk=to_np(pick(ix.v_blocks)),
+               slot_token=to_np(pick(ix.slot_token)), steady_k=to_np(pick(ix.steady_k)),
+               steady_v=to_np(pick(ix.steady_v)), assign=to_np(pick(ix.assign)))
+    if ix.pend_k is not None:
+        out["pend_k"] = to_np(pick(ix.pend_k))
+        out["pend_v"] = to_np(pick(ix.pend_v))
+    return out
 
 
 def assert_index_equal(got: dict, ref: dict, units=None, n_st=68):

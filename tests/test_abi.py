@@ -205,3 +205,59 @@ def test_noalloc_validates_like_the_workspace_entry_point(L):
     rc = L.wi_decode_attention_noalloc(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(bufs),
                                        fake, fake, None, None, None, 0, None)
     assert rc == 2
+
+
+@pytest.mark.parametrize("N,pend", [(68 + 3 * 96 + 41 + 50, 50), (68 + 2 * 96 + 96, 96),
+                                    (68 + 96 + 1, 1)])
+def test_sizes_with_pending_tokens_match_oracle(L, N, pend):
+    d = wi.make_desc("bf16", 1, 2, N, seg_len=96, clusters_per_seg=12)
+    d.n_pending = pend
+    od = oracle.make_desc("bf16", 1, 2, N, seg_len=96, clusters_per_seg=12, n_pending=pend)
+    assert wi.index_sizes(d)[:3] == oracle.sizes(od)[:3]
+
+
+def test_growth_calls_reject_invalid_descriptors(L):
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced
+    bufs = wi.IndexBufs(*([0x100000] * 12))
+    d = wi.make_desc("bf16", 1, 2, 68 + 96 + 96, seg_len=96, clusters_per_seg=12)
+    d.n_pending = 97  # beyond seg_len
+    assert L.wi_append_token(ctypes.byref(d), ctypes.byref(bufs), fake, fake, None) == 1
+    d.n_pending = 96  # full: cluster the segment before the next append
+    assert L.wi_append_token(ctypes.byref(d), ctypes.byref(bufs), fake, fake, None) == 1
+    assert b"wi_extend_index" in L.wi_last_error()
+    d.n_pending = 10
+    nopend = wi.IndexBufs(*([0x100000] * 10))
+    assert L.wi_append_token(ctypes.byref(d), ctypes.byref(nopend), fake, fake, None) == 1
+    assert b"pend_k" in L.wi_last_error()
+    assert L.wi_append_token(ctypes.byref(d), ctypes.byref(bufs), None, fake, None) == 1
+    ws = ctypes.c_size_t()
+    assert L.wi_extend_sizes(ctypes.byref(d), ctypes.byref(ws)) == 1  # not full
+    rc = L.wi_extend_index(ctypes.byref(d), ctypes.byref(bufs), ctypes.byref(bufs), fake,
+                           1 << 40, None)
+    assert rc == 1
+    d.n_ctx = 68 + 96  # too short for 96 pending tokens plus one clustered token
+    d.n_pending = 96
+    assert L.wi_extend_sizes(ctypes.byref(d), ctypes.byref(ws)) == 1
+    # a pending descriptor is not a build descriptor
+    d2 = wi.make_desc("bf16", 1, 2, 68 + 96 + 5, seg_len=96, clusters_per_seg=12)
+    d2.n_pending = 5
+    need = wi.index_sizes(d2)[3]
+    rc = L.wi_build_index(ctypes.byref(d2), fake, fake, None, ctypes.byref(bufs), fake, need,
+                          None)
+    assert rc == 1 and b"n_pending" in L.wi_last_error()
+
+
+def test_extend_workspace_holds_a_one_segment_build(L):
+    d = wi.make_desc("bf16", 1, 8, 131072 + 8192)
+    d.n_pending = 8192
+    ws = wi.extend_sizes(d)
+    seg = wi.make_desc("bf16", 1, 8, 8192, n_sink=0, n_local=0)
+    ns, C, cap, bws = wi.index_sizes(seg)
+    index_bytes = 8 * (C * 128 * 2 + C * 4 + C * 128 * 4 + (C + 1) * 4 + 2 * cap * 8 * 128 * 2
+                       + cap * 8 * 4 + 8192 * 4)
+    assert ws >= bws + index_bytes
+    fake = ctypes.c_void_p(0x100000)
+    bufs = wi.IndexBufs(*([0x100000] * 12))
+    rc = L.wi_extend_index(ctypes.byref(d), ctypes.byref(bufs), ctypes.byref(bufs), fake,
+                           ws - 1, None)
+    assert rc == 3
