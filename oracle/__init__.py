@@ -14,8 +14,13 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "libwi_oracle.so")
 _SRC = os.path.join(_HERE, "wi_oracle.c")
+# WIO_SANITIZE=1 selects a separate build instrumented with AddressSanitizer
+# and UndefinedBehaviorSanitizer (load it with libasan preloaded).
+SANITIZE = os.environ.get("WIO_SANITIZE") == "1"
+_SO = os.path.join(_HERE, "libwi_oracle_san.so" if SANITIZE else "libwi_oracle.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"]
 
 F32, BF16 = 0, 1
 
@@ -37,8 +42,9 @@ def gcc_command(src: str, out: str) -> list:
     rounded either way; -mfma (where the host has it) only lets gcc emit the
     instruction instead of a libm call."""
     fma = ["-mfma"] if _host_has_fma() else []
+    san = SANITIZE_FLAGS if SANITIZE else []
     return ["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-            *fma, "-fPIC", "-shared", src, "-o", out, "-lm"]
+            *fma, *san, "-fPIC", "-shared", src, "-o", out, "-lm"]
 
 
 def _flags() -> str:

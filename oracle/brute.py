@@ -81,13 +81,16 @@ def full_attention(q, K, V, scale):
     return softmax_list(q, K, V, np.ones(K.shape[0]), scale)
 
 
-def tripartite(q, K, V, members, centroids, R, E, n_sink, n_local, scale, extra=()):
+def tripartite(q, K, V, members, centroids, R, E, n_sink, n_local, scale, extra=(),
+               vsum_f32=False):
     """Explicit-list tripartite attention for one query head.
 
     members[c]: token positions of cluster c. Steady tokens, the extra exact
     positions (pending decode-time tokens) and every token of the R clusters
     are listed as themselves; each non-empty E cluster is one entry with
-    key = centroid, value = mean member value, multiplicity n_c.
+    key = centroid, value = mean member value, multiplicity n_c. With
+    vsum_f32 the members' value sum is first rounded to float32, the
+    precision an index stores it in.
     """
     n = K.shape[0]
     steady = list(range(n_sink)) + list(range(n - n_local, n))
@@ -100,7 +103,10 @@ def tripartite(q, K, V, members, centroids, R, E, n_sink, n_local, scale, extra=
         if len(m) == 0:
             continue
         keys.append(centroids[c][None, :])
-        vals.append(V[m].astype(np.float64).mean(0)[None, :])
+        vs = V[m].astype(np.float64).sum(0)
+        if vsum_f32:
+            vs = vs.astype(np.float32).astype(np.float64)
+        vals.append((vs / len(m))[None, :])
         mult.append(np.array([float(len(m))]))
     return softmax_list(q, np.concatenate(keys), np.concatenate(vals),
                         np.concatenate(mult), scale)
