@@ -107,6 +107,8 @@ def lib():
         _lib.wio_attend_sets.argtypes = [P] * 13 + [P, i32, P, i32, P]
         _lib.wio_append.argtypes = [P] * 7
         _lib.wio_extend.argtypes = [P] * 23
+        _lib.wio_dense_attention.argtypes = [P] * 6
+        _lib.wio_recall.argtypes = [P] * 8 + [i32, i32, P, P, P]
         _lib.wio_num_threads.restype = ctypes.c_int
     return _lib
 
@@ -315,6 +317,41 @@ def extend(desc, idx):
     if rc != 0:
         raise ValueError("oracle extend failed (pending segment not full?)")
     return nd, out
+
+
+def dense_attention(desc, n_q_heads, K, V, q, scale=0.0):
+    """Full attention over all desc.n_ctx tokens (float64): K, V [B, H, N, d]."""
+    K = np.ascontiguousarray(K, dtype=np.float32)
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    assert K.shape == (desc.batch, desc.n_kv_heads, desc.n_ctx, desc.head_dim)
+    out = np.empty((desc.batch, n_q_heads, desc.head_dim), np.float64)
+    dd = DDesc(n_q_heads, 0, 0, scale)
+    rc = lib().wio_dense_attention(ctypes.byref(desc), ctypes.byref(dd), _p(K), _p(V), _p(q),
+                                   _p(out))
+    if rc != 0:
+        raise ValueError("oracle dense attention failed")
+    return out
+
+
+def recall(desc, n_q_heads, idx, q, R, k):
+    """recall@k of the retrieval zone R [U, n_r]: dict(recall [B, Hq],
+    top [B, Hq, k] positions, top_score [B, Hq, k])."""
+    U = desc.batch * desc.n_kv_heads
+    R = np.ascontiguousarray(R, dtype=np.int32).reshape(U, -1)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    res = dict(recall=np.empty((desc.batch, n_q_heads), np.float64),
+               top=np.empty((desc.batch, n_q_heads, k), np.int32),
+               top_score=np.empty((desc.batch, n_q_heads, k), np.float64))
+    dd = DDesc(n_q_heads, 0, 0, 0.0)
+    keep = [np.ascontiguousarray(idx[key]) for key in ("sizes", "block_off", "kblk",
+                                                       "slot_token")]
+    rc = lib().wio_recall(ctypes.byref(desc), ctypes.byref(dd), *[_p(a) for a in keep], _p(q),
+                          _p(R), R.shape[1], k, _p(res["recall"]), _p(res["top"]),
+                          _p(res["top_score"]))
+    if rc != 0:
+        raise ValueError("oracle recall failed (k outside [1, clustered tokens]?)")
+    return res
 
 
 def num_threads() -> int:

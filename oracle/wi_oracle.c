@@ -723,4 +723,123 @@ int wio_extend(const wio_desc *d, const float *centroids, const int32_t *sizes,
   return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Per-layer zone policy pieces. [blog] 3.3 (layer-wise strategy for very
+ * large models): the lower layers keep full attention for precise
+ * localisation, the middle layers use the hybrid scheme, the upper layers
+ * raise the estimation share (to 30 %). [blog] 4.3 problem 3: sparse
+ * attention is switched off in the first two layers. [blog] 4.3 problem 1:
+ * the clustering's recall@100 should exceed 0.85. */
+
+/* Dense decode attention over all N context tokens, per query head j of KV
+ * head h (standard grouped-query mapping, h = j / G):
+ *   o_j = sum_i e^{z_i - m} v_i / sum_i e^{z_i - m},  z_i = scale <q_j, k_i>,
+ * m = max_i z_i, all in float64. K, V: [B][H][N][d]; q: [B][Hq][d];
+ * out: [B][Hq][d]. */
+int wio_dense_attention(const wio_desc *d, const wio_ddesc *dd, const float *K,
+                        const float *V, const float *q, double *out) {
+  if (dd->n_q_heads % d->n_kv_heads != 0 || d->n_ctx < 1) return -1;
+  const int D = d->head_dim;
+  const int G = dd->n_q_heads / d->n_kv_heads;
+  const int64_t N = d->n_ctx;
+  const double scale = dd->scale > 0 ? dd->scale : 1.0 / sqrt((double)D);
+  const int64_t U = (int64_t)d->batch * d->n_kv_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < U; u++) {
+    const int64_t b = u / d->n_kv_heads, h = u % d->n_kv_heads;
+    const float *Ku = K + (size_t)u * N * D;
+    const float *Vu = V + (size_t)u * N * D;
+    for (int j = 0; j < G; j++) {
+      const float *qh = q + ((size_t)b * dd->n_q_heads + (size_t)h * G + j) * D;
+      double *o = out + ((size_t)b * dd->n_q_heads + (size_t)h * G + j) * D;
+      double m = -INFINITY;
+      for (int64_t i = 0; i < N; i++) {
+        const double z = dot64(qh, Ku + (size_t)i * D, D) * scale;
+        if (z > m) m = z;
+      }
+      double den = 0.0;
+      for (int t = 0; t < D; t++) o[t] = 0.0;
+      for (int64_t i = 0; i < N; i++) {
+        const double p = exp(dot64(qh, Ku + (size_t)i * D, D) * scale - m);
+        den += p;
+        for (int t = 0; t < D; t++) o[t] += p * (double)Vu[(size_t)i * D + t];
+      }
+      for (int t = 0; t < D; t++) o[t] /= den;
+    }
+  }
+  return 0;
+}
+
+typedef struct { double s; int32_t pos; int32_t c; } scored;
+
+/* Token order for recall: larger score first, equal scores by lower
+ * position. */
+static int scored_cmp(const void *pa, const void *pb) {
+  const scored *a = (const scored *)pa, *b = (const scored *)pb;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return (a->pos > b->pos) - (a->pos < b->pos);
+}
+
+/* recall@k of a retrieval zone. Reading of "recall@100" ([blog] 4.3 problem
+ * 1): for query head j of unit u, take the k clustered tokens with the
+ * largest exact attention scores <q_j, k_i> (the tokens attention weights
+ * most; equal scores by lower position) and count the share of them that
+ * belong to a cluster of the unit's retrieval zone R_u. Steady and pending
+ * tokens are attended exactly anyway and are not part of the measure. The
+ * keys are read from the index's blocks (each clustered token once).
+ *   R: [U][n_r] cluster ids; recall: [B][Hq]; top (optional): [B][Hq][k]
+ *   positions in rank order; top_score (optional): their scores <q_j, k_i>.
+ * Returns -1 when k < 1 or k exceeds the clustered token count. */
+int wio_recall(const wio_desc *d, const wio_ddesc *dd, const int32_t *sizes,
+               const int32_t *block_off, const float *kblk,
+               const int32_t *slot_token, const float *q, const int32_t *R,
+               int32_t n_r, int32_t k, double *recall, int32_t *top,
+               double *top_score) {
+  int64_t ns, C, cap;
+  int32_t T;
+  if (wio_sizes(d, &ns, &C, &cap, &T) != 0) return -1;
+  if (dd->n_q_heads % d->n_kv_heads != 0) return -1;
+  const int64_t n_idx = idx_count(d);
+  if (k < 1 || k > n_idx) return -1;
+  const int D = d->head_dim;
+  const int G = dd->n_q_heads / d->n_kv_heads;
+  const int64_t U = (int64_t)d->batch * d->n_kv_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < U; u++) {
+    const int64_t b = u / d->n_kv_heads, h = u % d->n_kv_heads;
+    const int32_t *bo = block_off + (size_t)u * (C + 1);
+    const int32_t *cnt = sizes + (size_t)u * C;
+    const int32_t *st = slot_token + (size_t)u * cap * T;
+    const float *kb = kblk + (size_t)u * cap * T * D;
+    unsigned char *inR = (unsigned char *)calloc((size_t)C, 1);
+    for (int r = 0; r < n_r; r++) inR[R[(size_t)u * n_r + r]] = 1;
+    scored *all = (scored *)malloc(sizeof(scored) * (size_t)n_idx);
+    for (int j = 0; j < G; j++) {
+      const size_t qi = (size_t)b * dd->n_q_heads + (size_t)h * G + j;
+      const float *qh = q + qi * D;
+      int64_t n = 0;
+      for (int64_t c = 0; c < C; c++)
+        for (int32_t i = 0; i < cnt[c]; i++) {
+          const int64_t slot = (int64_t)bo[c] * T + i;
+          all[n].s = dot64(qh, kb + slot * D, D);
+          all[n].pos = st[slot];
+          all[n].c = (int32_t)c;
+          n++;
+        }
+      qsort(all, (size_t)n, sizeof(scored), scored_cmp);
+      int hit = 0;
+      for (int32_t i = 0; i < k; i++) {
+        hit += inR[all[i].c];
+        if (top) top[qi * k + i] = all[i].pos;
+        if (top_score) top_score[qi * k + i] = all[i].s;
+      }
+      recall[qi] = (double)hit / (double)k;
+    }
+    free(all);
+    free(inR);
+  }
+  return 0;
+}
+
 int wio_num_threads(void) { return omp_get_max_threads(); }

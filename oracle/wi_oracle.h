@@ -142,6 +142,23 @@ int wio_extend(const wio_desc *d, const float *centroids, const int32_t *sizes,
                int32_t *n_slot_token, float *n_steady_k, float *n_steady_v,
                int32_t *n_assign);
 
+/* ---- per-layer policy pieces --------------------------------------- */
+/* Dense decode attention over all n_ctx tokens, float64 (the full-attention
+ * layers of the per-layer zone policy). K, V: [B][H][N][d]; q, out:
+ * [B][Hq][d]. */
+int wio_dense_attention(const wio_desc *d, const wio_ddesc *dd, const float *K,
+                        const float *V, const float *q, double *out);
+
+/* recall@k of a retrieval zone R ([U][n_r] cluster ids): per query head, the
+ * share of the k clustered tokens with the largest exact scores (ties to the
+ * lower position) that lie in R's clusters. recall: [B][Hq]; top / top_score
+ * (optional): [B][Hq][k] positions in rank order and their scores. */
+int wio_recall(const wio_desc *d, const wio_ddesc *dd, const int32_t *sizes,
+               const int32_t *block_off, const float *kblk,
+               const int32_t *slot_token, const float *q, const int32_t *R,
+               int32_t n_r, int32_t k, double *recall, int32_t *top,
+               double *top_score);
+
 int wio_num_threads(void);
 
 #ifdef __cplusplus
