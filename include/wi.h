@@ -247,6 +247,76 @@ wi_status wi_extend_index(const wi_index_desc *desc, const wi_index_bufs *bufs,
                           const wi_index_bufs *new_bufs, void *ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* ---- per-layer zone policy ------------------------------------------ */
+/* framerc blog section 3.3 (layer-wise strategy, given for an 80-layer
+ * model): layers 0-20 keep full attention for precise localisation, layers
+ * 21-60 use the hybrid scheme, the upper layers raise the estimation share
+ * to 30 %. Section 4.3, problem 3: sparse attention switched off in the
+ * first two layers. Section 2.1: hybrid budgets of about 1.8 % retrieved and
+ * 23 % estimated tokens. */
+enum { WI_LAYER_DENSE = 0, WI_LAYER_HYBRID = 1 };
+enum {
+  WI_POLICY_UNIFORM = 0,      /* every layer hybrid (1.8 %, 23 %)            */
+  WI_POLICY_DENSE_FIRST2 = 1, /* layers 0 and 1 dense, the rest hybrid       */
+  WI_POLICY_BANDED = 2        /* dense if 80 l < 21 L; hybrid with a 30 %
+                                 estimation share if 80 l >= 61 L; else
+                                 hybrid (the 80-layer bands as fractions of
+                                 depth L)                                    */
+};
+
+/* Host-only: the plan of layer `layer` of an n_layers-layer model at n_ctx
+ * tokens: *mode (WI_LAYER_DENSE or WI_LAYER_HYBRID) and, for hybrid layers,
+ * the cluster budgets round(f * n_ctx * clusters_per_seg / seg_len) for the
+ * token shares f (0 and 0 for dense layers). Any output may be NULL.
+ * WI_E_INVALID for an unknown policy or a layer outside [0, n_layers). */
+wi_status wi_layer_plan(int32_t policy, int32_t layer, int32_t n_layers,
+                        int64_t n_ctx, int32_t seg_len, int32_t clusters_per_seg,
+                        int32_t *mode, int32_t *k_retrieve, int32_t *k_estimate);
+
+/* Host-only: workspace bytes of wi_dense_attention. */
+wi_status wi_dense_sizes(const wi_index_desc *desc,
+                         const wi_decode_desc *ddesc, size_t *workspace_bytes);
+
+/* Dense decode attention, for the layers a policy keeps dense: every one of
+ * the n_ctx tokens is attended by each query head of its KV head,
+ *   out_j = sum_i e^{z_i} v_i / sum_i e^{z_i},  z_i = scale <q_j, k_i>.
+ * Only desc's dtype, batch, n_kv_heads, head_dim (128), n_ctx (>= 1) and
+ * K/V strides are read; ddesc's n_q_heads and scale (0 -> 1/sqrt(128)).
+ *   k, v   device [B][H][N][128] dtype, strides from desc
+ *   q      device [B][Hq][128] dtype
+ *   out    device [B][Hq][128] float32
+ *   ws     device workspace of wi_dense_sizes bytes (chunk partials) */
+wi_status wi_dense_attention(const wi_index_desc *desc,
+                             const wi_decode_desc *ddesc, const void *k,
+                             const void *v, const void *q, float *out,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Host-only: workspace bytes of wi_recall_at_k (8 bytes per used slot of
+ * every query head). */
+wi_status wi_recall_sizes(const wi_index_desc *desc,
+                          const wi_decode_desc *ddesc, size_t *workspace_bytes);
+
+/* recall@k of a retrieval zone (framerc blog section 4.3, problem 1: the
+ * clustering's recall@100 should exceed 0.85). For each query head j: the k
+ * clustered tokens with the largest scores <q_j, k_i> (float32 from the
+ * index's key blocks; equal scores by lower position) and the share of them
+ * whose cluster is in the unit's retrieval zone.
+ *   bufs        the index (block_off, k_blocks, slot_token, assign)
+ *   q           device [B][Hq][128] dtype
+ *   sel_ids     device, unit u's retrieval zone is sel_ids[u * sel_stride
+ *               .. + n_r) (e.g. the first K_r ids of wi_decode_attention's
+ *               sel_ids, sel_stride = K_r + K_e')
+ *   k           1 .. min(1024, clustered tokens)
+ *   recall      device [B][Hq] float32
+ *   top_tokens  device [B][Hq][k] int32 positions in rank order, or NULL
+ *   ws          device workspace of wi_recall_sizes bytes */
+wi_status wi_recall_at_k(const wi_index_desc *desc, const wi_decode_desc *ddesc,
+                         const wi_index_bufs *bufs, const void *q,
+                         const int32_t *sel_ids, int32_t sel_stride,
+                         int32_t n_r, int32_t k, float *recall,
+                         int32_t *top_tokens, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* Largest decode workspace that wi_decode_attention_noalloc serves: 16 MiB
  * (the five model shapes of this library need at most 11.5 MiB: 8 units of
  * 65536 clusters, or 64 units of 8192). */

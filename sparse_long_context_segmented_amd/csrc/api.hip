@@ -270,7 +270,7 @@ thread_local int t_cur = -1;
 const char* const kNames[wi::K_COUNT] = {
     "zero", "copy_init", "kpp_init", "kpp_weights", "kpp_round", "assign", "assign_fix",
     "sort_update", "seg_scan", "layout", "score", "select_attend", "rank", "exec", "append",
-    "merge"};
+    "merge", "dense", "dense_merge", "recall"};
 
 hipEvent_t take_event() {
   if (!t_pool.empty()) {
@@ -613,6 +613,173 @@ wi_status wi_extend_index(const wi_index_desc* desc, const wi_index_bufs* bufs,
   st = run_build(gs, bufs->pend_k, bufs->pend_v, nullptr, sb, w, stream);
   if (st != WI_OK) return st;
   CHECK_HIP(wi::launch_extend_merge(g, gn, gs, *bufs, sb, *new_bufs, stream), "merge");
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_layer_plan(int32_t policy, int32_t layer, int32_t n_layers, int64_t n_ctx,
+                        int32_t seg_len, int32_t clusters_per_seg, int32_t* mode,
+                        int32_t* k_retrieve, int32_t* k_estimate) {
+  if (n_layers < 1 || layer < 0 || layer >= n_layers)
+    return fail(WI_E_INVALID, "layer %d outside [0, n_layers = %d)", layer, n_layers);
+  if (n_ctx < 1 || seg_len < 1 || clusters_per_seg < 1)
+    return fail(WI_E_INVALID, "n_ctx, seg_len and clusters_per_seg must be >= 1");
+  bool dense, upper;
+  switch (policy) {
+    case WI_POLICY_UNIFORM: dense = false; upper = false; break;
+    case WI_POLICY_DENSE_FIRST2: dense = layer < 2; upper = false; break;
+    case WI_POLICY_BANDED:
+      dense = 80ll * layer < 21ll * n_layers;
+      upper = 80ll * layer >= 61ll * n_layers;
+      break;
+    default: return fail(WI_E_INVALID, "unknown policy %d", policy);
+  }
+  // a token share f is f * n_ctx * clusters_per_seg / seg_len clusters, rounded half up
+  auto clusters = [&](double f) {
+    return (int32_t)std::floor(f * (double)n_ctx * (double)clusters_per_seg / (double)seg_len + 0.5);
+  };
+  if (mode) *mode = dense ? WI_LAYER_DENSE : WI_LAYER_HYBRID;
+  if (k_retrieve) *k_retrieve = dense ? 0 : clusters(0.018);
+  if (k_estimate) *k_estimate = dense ? 0 : clusters(upper ? 0.30 : 0.23);
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shapes of a dense call: the K/V layout fields of the index descriptor and
+// the head mapping of the decode descriptor.
+struct DenseShape {
+  int dtype, B, H, U, Hq, G;
+  int64_t N, sb, sh, st;
+  float scale;
+  int W;
+};
+
+wi_status make_dense(const wi_index_desc* d, const wi_decode_desc* dd, DenseShape* o) {
+  if (!d || !dd) return fail(WI_E_INVALID, "descriptor is NULL");
+  if (d->dtype != WI_F32 && d->dtype != WI_BF16)
+    return fail(WI_E_UNSUPPORTED, "unknown dtype %d", d->dtype);
+  if (d->head_dim != wi::D) return fail(WI_E_UNSUPPORTED, "head_dim %d != 128", d->head_dim);
+  if (d->batch < 1 || d->n_kv_heads < 1)
+    return fail(WI_E_INVALID, "batch %d / n_kv_heads %d must be >= 1", d->batch, d->n_kv_heads);
+  if (d->n_ctx < 1 || d->n_ctx >= (int64_t(1) << 31))
+    return fail(WI_E_INVALID, "n_ctx %lld outside [1, 2^31)", (long long)d->n_ctx);
+  if (d->kv_stride_t <= 0 || d->kv_stride_h < 0 || d->kv_stride_b < 0 ||
+      d->kv_stride_t % 8 || d->kv_stride_h % 8 || d->kv_stride_b % 8)
+    return fail(WI_E_INVALID, "K/V strides must be non-negative multiples of 8 (t > 0)");
+  if (dd->n_q_heads < 1 || dd->n_q_heads % d->n_kv_heads)
+    return fail(WI_E_UNSUPPORTED, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                dd->n_q_heads, d->n_kv_heads);
+  const int G = dd->n_q_heads / d->n_kv_heads;
+  if (G > wi::MAX_G) return fail(WI_E_UNSUPPORTED, "%d query heads per KV head > %d", G, wi::MAX_G);
+  if (!(dd->scale >= 0.f) || !std::isfinite(dd->scale))
+    return fail(WI_E_INVALID, "scale must be finite and >= 0");
+  o->dtype = d->dtype;
+  o->B = d->batch;
+  o->H = d->n_kv_heads;
+  o->U = d->batch * d->n_kv_heads;
+  o->Hq = dd->n_q_heads;
+  o->G = G;
+  o->N = d->n_ctx;
+  o->sb = d->kv_stride_b;
+  o->sh = d->kv_stride_h;
+  o->st = d->kv_stride_t;
+  o->scale = dd->scale > 0.f ? dd->scale : 1.f / std::sqrt((float)wi::D);
+  o->W = wi::dense_chunks(o->U, o->N);
+  return WI_OK;
+}
+
+int64_t recall_ws_bytes(const wi::Geom& g, int G) {
+  return align256((int64_t)g.U * G * g.cap * g.T * 8);
+}
+
+}  // namespace
+
+extern "C" {
+
+wi_status wi_dense_sizes(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                         size_t* workspace_bytes) {
+  DenseShape ds;
+  wi_status st = make_dense(desc, ddesc, &ds);
+  if (st != WI_OK) return st;
+  if (workspace_bytes)
+    *workspace_bytes = (size_t)align256(wi::dense_part_floats(ds.U, ds.W, ds.G) * 4);
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_dense_attention(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                             const void* k, const void* v, const void* q, float* out, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  DenseShape ds;
+  wi_status st = make_dense(desc, ddesc, &ds);
+  if (st != WI_OK) return st;
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(q, "q");
+  CHECK_PTR(out, "out");
+  const int64_t need = align256(wi::dense_part_floats(ds.U, ds.W, ds.G) * 4);
+  if (!ws || (int64_t)ws_bytes < need)
+    return fail(WI_E_WORKSPACE, "workspace %zu bytes < %lld required", ws_bytes, (long long)need);
+  if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
+  CHECK_HIP(wi::launch_dense(ds.dtype, ds.B, ds.H, ds.Hq, ds.G, ds.N, ds.sb, ds.sh, ds.st,
+                             ds.scale, k, v, q, out, reinterpret_cast<float*>(ws), stream),
+            "dense attention");
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_recall_sizes(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                          size_t* workspace_bytes) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  if (!ddesc) return fail(WI_E_INVALID, "decode desc is NULL");
+  if (ddesc->n_q_heads < 1 || ddesc->n_q_heads % g.H)
+    return fail(WI_E_UNSUPPORTED, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                ddesc->n_q_heads, g.H);
+  const int G = ddesc->n_q_heads / g.H;
+  if (G > wi::MAX_G) return fail(WI_E_UNSUPPORTED, "%d query heads per KV head > %d", G, wi::MAX_G);
+  if (workspace_bytes) *workspace_bytes = (size_t)recall_ws_bytes(g, G);
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_recall_at_k(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                         const wi_index_bufs* bufs, const void* q, const int32_t* sel_ids,
+                         int32_t sel_stride, int32_t n_r, int32_t k, float* recall,
+                         int32_t* top_tokens, void* ws, size_t ws_bytes, hipStream_t stream) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  size_t need = 0;
+  st = wi_recall_sizes(desc, ddesc, &need);
+  if (st != WI_OK) return st;
+  const int G = ddesc->n_q_heads / g.H;
+  if (k < 1 || k > wi::recall_max_k() || (int64_t)k > g.n_idx)
+    return fail(WI_E_INVALID, "k %d outside [1, min(%d, clustered tokens %lld)]", k,
+                wi::recall_max_k(), (long long)g.n_idx);
+  if (n_r < 0 || n_r > g.C) return fail(WI_E_INVALID, "n_r %d outside [0, C = %d]", n_r, g.C);
+  if (sel_stride < n_r) return fail(WI_E_INVALID, "sel_stride %d < n_r %d", sel_stride, n_r);
+  if (n_r > 0) CHECK_PTR(sel_ids, "sel_ids");
+  if (!bufs) return fail(WI_E_INVALID, "bufs is NULL");
+  CHECK_PTR(bufs->block_off, "bufs->block_off");
+  CHECK_PTR(bufs->k_blocks, "bufs->k_blocks");
+  CHECK_PTR(bufs->slot_token, "bufs->slot_token");
+  CHECK_PTR(bufs->assign, "bufs->assign");
+  CHECK_PTR(q, "q");
+  CHECK_PTR(recall, "recall");
+  if (top_tokens && !aligned16(top_tokens))
+    return fail(WI_E_INVALID, "top_tokens is not 16-byte aligned");
+  if (!ws || ws_bytes < need)
+    return fail(WI_E_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+  if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
+  CHECK_HIP(wi::launch_recall(g, ddesc->n_q_heads, G, *bufs, q, sel_ids, sel_stride, n_r, k,
+                              recall, top_tokens, reinterpret_cast<uint64_t*>(ws), stream),
+            "recall");
   g_err[0] = 0;
   return WI_OK;
 }

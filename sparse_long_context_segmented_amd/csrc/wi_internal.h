@@ -191,7 +191,7 @@ __device__ __forceinline__ float wave_max(float v) {
 enum KernelId {
   K_ZERO, K_COPY, K_KPP_INIT, K_KPP_WEIGHTS, K_KPP_ROUND, K_ASSIGN, K_ASSIGN_FIX,
   K_SORT_UPDATE, K_SEG_SCAN, K_LAYOUT, K_SCORE, K_FUSED, K_RANK,
-  K_EXEC, K_APPEND, K_MERGE, K_COUNT
+  K_EXEC, K_APPEND, K_MERGE, K_DENSE, K_DENSE_MERGE, K_RECALL, K_COUNT
 };
 void tmark_begin(KernelId id, hipStream_t s);
 void tmark_end(hipStream_t s);
@@ -240,6 +240,18 @@ hipError_t launch_append(const Geom& g, const wi_index_bufs& b, const void* k_ne
 hipError_t launch_extend_merge(const Geom& go, const Geom& gn, const Geom& gs,
                                const wi_index_bufs& o, const wi_index_bufs& sg,
                                const wi_index_bufs& nw, hipStream_t s);
+// Dense decode attention (full-attention layers): chunks per unit, partial
+// buffer size in floats, and the two launches.
+int dense_chunks(int U, int64_t N);
+int64_t dense_part_floats(int U, int W, int G);
+hipError_t launch_dense(int dtype, int B, int H, int Hq, int G, int64_t N, int64_t sb,
+                        int64_t sh, int64_t st, float scale, const void* k, const void* v,
+                        const void* q, float* out, float* part, hipStream_t s);
+// recall@k: largest k served; keys is [U][G][cap*T] uint64 scratch.
+int recall_max_k();
+hipError_t launch_recall(const Geom& g, int Hq, int G, const wi_index_bufs& bf, const void* q,
+                         const int32_t* sel, int sel_stride, int n_r, int k, float* recall,
+                         int32_t* top, uint64_t* keys, hipStream_t s);
 hipError_t launch_debug_outputs(const DecodeArgs& a, const wi_index_bufs& b,
                                 const DecodeWs& ws, int32_t* sel_ids,
                                 int32_t* exec_tokens, int32_t* n_exec,

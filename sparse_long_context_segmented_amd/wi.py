@@ -17,11 +17,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libwi.so")
 
 WI_F32, WI_BF16 = 0, 1
+WI_LAYER_DENSE, WI_LAYER_HYBRID = 0, 1
+WI_POLICY_UNIFORM, WI_POLICY_DENSE_FIRST2, WI_POLICY_BANDED = 0, 1, 2
 STATUS = {0: "WI_OK", 1: "WI_E_INVALID", 2: "WI_E_UNSUPPORTED", 3: "WI_E_WORKSPACE",
           4: "WI_E_HIP"}
 EXPORTS = ("wi_index_sizes", "wi_build_index", "wi_decode_sizes", "wi_decode_attention",
            "wi_decode_attention_noalloc", "wi_append_token", "wi_extend_sizes",
-           "wi_extend_index", "wi_status_str", "wi_last_error",
+           "wi_extend_index", "wi_layer_plan", "wi_dense_sizes", "wi_dense_attention",
+           "wi_recall_sizes", "wi_recall_at_k", "wi_status_str", "wi_last_error",
            "wi_timing_start", "wi_timing_stop", "wi_kernel_name")
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -84,6 +87,17 @@ def lib():
         L.wi_extend_sizes.restype = ctypes.c_int
         L.wi_extend_index.argtypes = [P, P, P, P, ctypes.c_size_t, P]
         L.wi_extend_index.restype = ctypes.c_int
+        i32 = ctypes.c_int32
+        L.wi_layer_plan.argtypes = [i32, i32, i32, ctypes.c_int64, i32, i32, P, P, P]
+        L.wi_layer_plan.restype = ctypes.c_int
+        L.wi_dense_sizes.argtypes = [P, P, P]
+        L.wi_dense_sizes.restype = ctypes.c_int
+        L.wi_dense_attention.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.wi_dense_attention.restype = ctypes.c_int
+        L.wi_recall_sizes.argtypes = [P, P, P]
+        L.wi_recall_sizes.restype = ctypes.c_int
+        L.wi_recall_at_k.argtypes = [P, P, P, P, P, i32, i32, i32, P, P, P, ctypes.c_size_t, P]
+        L.wi_recall_at_k.restype = ctypes.c_int
         L.wi_status_str.argtypes = [ctypes.c_int]
         L.wi_status_str.restype = ctypes.c_char_p
         L.wi_last_error.argtypes = []
@@ -295,6 +309,61 @@ def extend_index(index: Index, ws: torch.Tensor | None = None, new: Index | None
     _check(lib().wi_extend_index(ctypes.byref(desc), ctypes.byref(ob), ctypes.byref(nb),
                                  _ptr(ws), ws.numel(), _stream(stream)))
     return new
+
+
+def layer_plan(policy: int, layer: int, n_layers: int, n_ctx: int, seg_len: int = 8192,
+               clusters_per_seg: int = 512):
+    """(mode, k_retrieve, k_estimate) of one layer under a per-layer policy."""
+    m, kr, ke = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().wi_layer_plan(policy, layer, n_layers, n_ctx, seg_len, clusters_per_seg,
+                               ctypes.byref(m), ctypes.byref(kr), ctypes.byref(ke)))
+    return m.value, kr.value, ke.value
+
+
+def dense_sizes(desc: IndexDesc, ddesc: DecodeDesc) -> int:
+    ws = ctypes.c_size_t()
+    _check(lib().wi_dense_sizes(ctypes.byref(desc), ctypes.byref(ddesc), ctypes.byref(ws)))
+    return ws.value
+
+
+def dense_attention(desc: IndexDesc, ddesc: DecodeDesc, k: torch.Tensor, v: torch.Tensor,
+                    q: torch.Tensor, out: torch.Tensor | None = None,
+                    ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Run wi_dense_attention (k, v laid out as desc's strides say); returns
+    out [B, Hq, 128] float32."""
+    wsb = dense_sizes(desc, ddesc)
+    if out is None:
+        out = torch.empty(desc.batch, ddesc.n_q_heads, 128, dtype=torch.float32, device=q.device)
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().wi_dense_attention(ctypes.byref(desc), ctypes.byref(ddesc), _ptr(k), _ptr(v),
+                                    _ptr(q), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def recall_sizes(desc: IndexDesc, ddesc: DecodeDesc) -> int:
+    ws = ctypes.c_size_t()
+    _check(lib().wi_recall_sizes(ctypes.byref(desc), ctypes.byref(ddesc), ctypes.byref(ws)))
+    return ws.value
+
+
+def recall_at_k(index: Index, ddesc: DecodeDesc, q: torch.Tensor, sel_ids: torch.Tensor,
+                n_r: int, k: int = 100, want_top: bool = False, ws: torch.Tensor | None = None,
+                stream=None):
+    """Run wi_recall_at_k on the retrieval zone sel_ids[:, :n_r] ([U, stride]);
+    returns recall [B, Hq] float32 (and top [B, Hq, k] int32 with want_top)."""
+    desc = index.desc
+    wsb = recall_sizes(desc, ddesc)
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    rec = torch.empty(desc.batch, ddesc.n_q_heads, dtype=torch.float32, device=q.device)
+    top = (torch.empty(desc.batch, ddesc.n_q_heads, k, dtype=torch.int32, device=q.device)
+           if want_top else None)
+    bufs = index.bufs()
+    _check(lib().wi_recall_at_k(ctypes.byref(desc), ctypes.byref(ddesc), ctypes.byref(bufs),
+                                _ptr(q), _ptr(sel_ids), sel_ids.shape[-1], n_r, k, _ptr(rec),
+                                _ptr(top), _ptr(ws), ws.numel(), _stream(stream)))
+    return (rec, top) if want_top else rec
 
 
 def timing_start():

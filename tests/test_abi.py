@@ -261,3 +261,62 @@ def test_extend_workspace_holds_a_one_segment_build(L):
     rc = L.wi_extend_index(ctypes.byref(d), ctypes.byref(bufs), ctypes.byref(bufs), fake,
                            ws - 1, None)
     assert rc == 3
+
+
+@pytest.mark.parametrize("n_layers,n_ctx", [(80, 131072), (32, 1048576), (28, 262144),
+                                            (2, 8192), (1, 69)])
+def test_layer_plan_matches_oracle_policy(L, n_layers, n_ctx):
+    from oracle import policy
+    for kind in (policy.UNIFORM, policy.DENSE_FIRST2, policy.BANDED):
+        for layer in range(n_layers):
+            assert wi.layer_plan(kind, layer, n_layers, n_ctx) == \
+                policy.plan(kind, layer, n_layers, n_ctx), (kind, layer)
+
+
+def test_layer_plan_rejects_bad_arguments(L):
+    out = [ctypes.c_int32() for _ in range(3)]
+    refs = [ctypes.byref(o) for o in out]
+    assert L.wi_layer_plan(3, 0, 32, 131072, 8192, 512, *refs) == 1
+    assert L.wi_layer_plan(0, 32, 32, 131072, 8192, 512, *refs) == 1
+    assert L.wi_layer_plan(0, -1, 32, 131072, 8192, 512, *refs) == 1
+    assert L.wi_layer_plan(0, 0, 32, 0, 8192, 512, *refs) == 1
+    assert L.wi_layer_plan(2, 0, 32, 131072, 8192, 512, None, None, None) == 0
+
+
+def test_dense_and_recall_reject_invalid_calls(L):
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced
+    d = wi.make_desc("bf16", 1, 8, 131072)
+    dd = wi.DecodeDesc(32, 0, 0, 0.0)
+    need = wi.dense_sizes(d, dd)
+    assert need >= 8 * 4 * 130 * 4
+
+    def dense(desc=d, ddesc=dd, k=fake, v=fake, q=fake, out=fake, ws=fake, nb=need):
+        return L.wi_dense_attention(ctypes.byref(desc), ctypes.byref(ddesc), k, v, q, out, ws,
+                                    nb, None)
+    assert dense(k=None) == 1
+    assert dense(out=ctypes.c_void_p(0x100004)) == 1
+    assert dense(nb=need - 1) == 3
+    assert dense(ddesc=wi.DecodeDesc(30, 0, 0, 0.0)) == 2
+    bad = wi.make_desc("bf16", 1, 8, 131072)
+    bad.n_ctx = 0
+    assert dense(desc=bad) == 1
+    bad = wi.make_desc("bf16", 1, 8, 131072)
+    bad.head_dim = 64
+    assert dense(desc=bad) == 2
+    # recall: k range, zone size and pointers
+    bufs = wi.IndexBufs(*([0x100000] * 12))
+    wsr = wi.recall_sizes(d, dd)
+    assert wsr >= 8 * 4 * wi.index_sizes(d)[2] * 8 * 8
+
+    def rec(k=100, n_r=147, stride=2031, sel=fake, nb=wsr, b=bufs):
+        return L.wi_recall_at_k(ctypes.byref(d), ctypes.byref(dd), ctypes.byref(b), fake, sel,
+                                stride, n_r, k, fake, None, fake, nb, None)
+    assert rec(k=0) == 1
+    assert rec(k=1025) == 1
+    assert rec(n_r=8193) == 1
+    assert rec(stride=100) == 1
+    assert rec(sel=None) == 1
+    assert rec(nb=wsr - 1) == 3
+    nob = wi.IndexBufs(*([0x100000] * 12))
+    nob.assign = None
+    assert rec(b=nob) == 1
