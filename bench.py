@@ -141,15 +141,54 @@ def main():
                    "frac": round(assign_tflops / peak_mfma, 4),
                    "ms_per_launch": round(assign_ms, 4), "launches": n_assign},
     }
-    del kt, vt, ws_build
+    # ---- a dense layer of the same shape (the per-layer policy's full-
+    # attention layers): every token read once per query ----
+    ddn = wi.DecodeDesc(w.n_q_heads, 0, 0, 0.0)
+    wsdn = torch.empty(max(wi.dense_sizes(desc, ddn), 16), dtype=torch.uint8, device=dev)
+    outd = torch.empty(w.batch, w.n_q_heads, 128, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        wi.dense_attention(desc, ddn, kt, vt, qt, out=outd, ws=wsdn)
+    dense_reps = 20
+    ev0.record(stream)
+    for _ in range(dense_reps):
+        wi.dense_attention(desc, ddn, kt, vt, qt, out=outd, ws=wsdn)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = ev0.elapsed_time(ev1) / dense_reps
+    wi.timing_start()
+    for _ in range(dense_reps):
+        wi.dense_attention(desc, ddn, kt, vt, qt, out=outd, ws=wsdn)
+    drec = wi.timing_stop()
+    dk = {}
+    for name, ms in drec:
+        dk.setdefault(name, []).append(ms)
+    dense_kernel_ms = float(np.mean(dk["dense"]))
+    dense_bytes = U * w.n_ctx * 128 * e * 2 + w.batch * w.n_q_heads * 128 * (e + 4)
+    dense_gbs = dense_bytes / (dense_kernel_ms * 1e-3) / 1e9
+    policy = {"dense_layer": {
+        "ms_per_call": round(dense_ms, 4), "queries_per_s": round(w.batch / (dense_ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "dense", "achieved": round(dense_gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dense_gbs / PEAK_HBM_GBS, 4),
+                     "kernel_ms": {k: round(float(np.mean(v)), 5) for k, v in dk.items()},
+                     "algorithmic_bytes": int(dense_bytes)}}}
+    del kt, vt, ws_build, wsdn
 
     # ---- decode: R index copies at distinct addresses ----
     k_r, k_e = w.budgets()
     dd = wi.DecodeDesc(w.n_q_heads, k_r, k_e, 0.0, a.wg)
     nexe = torch.empty(U, dtype=torch.int32, device=dev)
-    wi.decode_attention(ix, dd, qt, n_exec=nexe)
+    sel = torch.empty(U, k_r + min(k_e, C - k_r), dtype=torch.int32, device=dev)
+    wi.decode_attention(ix, dd, qt, n_exec=nexe, sel_ids=sel)
     torch.cuda.synchronize()
     retrieved = int((nexe.cpu().numpy() - 68).sum())  # sum over units of sum_R n_c
+    # index-quality diagnostic: recall@100 of each query head's retrieval zone
+    k_rec = min(100, w.n_ctx - 68)
+    rec = wi.recall_at_k(ix, dd, qt, sel, k_r, k_rec).cpu().numpy()
+    policy["recall_at_100"] = {"k": k_rec, "min": round(float(rec.min()), 4),
+                               "mean": round(float(rec.mean()), 4),
+                               "query_heads": int(rec.size)}
+    del sel
     copies = [ix]
     for _ in range(a.instances - 1):
         copies.append(wi.Index(desc, *[getattr(ix, f).clone() for f in (
@@ -256,6 +295,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "build": build,
+        "policy": policy,
         "gen_s": round(gen_s, 1),
     }
 

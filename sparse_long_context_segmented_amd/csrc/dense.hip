@@ -12,9 +12,8 @@
 // heads as columns), updates a per-head online softmax, and adds
 // sum_i p_i v_i with each lane owning two value dimensions. The waves'
 // states are combined in LDS into one (m, l, acc[128]) partial per head and
-// chunk; a second kernel merges the chunks of each (unit, head). Occupancy,
-// not software pipelining, keeps loads in flight: every wave has a block of
-// loads outstanding while others compute.
+// chunk; a second kernel merges the chunks of each (unit, head). Each wave
+// issues the loads of its next block before computing the current one.
 #include "wi_internal.h"
 
 namespace wi {
@@ -63,13 +62,16 @@ __global__ __launch_bounds__(DN_THREADS) void dense_partial_kernel(
     }
   }
   __syncthreads();
+  // B operand: column r16 = query head r16 (columns >= GS repeat the last
+  // staged row and are masked with the heads >= G)
   uint4 bq[NKL];
+  const int qrow = r16 < GS ? r16 : GS - 1;
 #pragma unroll
   for (int s = 0; s < NKL; s++) {
     if constexpr (DT == WI_BF16)
-      bq[s] = *reinterpret_cast<const uint4*>(qs + (r16 * D + 32 * s + 8 * kg) * 2);
+      bq[s] = *reinterpret_cast<const uint4*>(qs + (qrow * D + 32 * s + 8 * kg) * 2);
     else
-      bq[s] = *reinterpret_cast<const uint4*>(qs + (r16 * D + 32 * kg + 4 * s) * 4);
+      bq[s] = *reinterpret_cast<const uint4*>(qs + (qrow * D + 32 * kg + 4 * s) * 4);
   }
 
   const int64_t t_lo = (int64_t)w * chunk;
@@ -83,49 +85,53 @@ __global__ __launch_bounds__(DN_THREADS) void dense_partial_kernel(
 #pragma unroll
   for (int g = 0; g < GS; g++) acc[g][0] = acc[g][1] = 0.f;
 
-#pragma unroll 1
-  for (int64_t t0 = t_lo + (int64_t)wv * TB; t0 < t_hi; t0 += (int64_t)DN_WAVES * TB) {
+  // one wave block: keys of tokens t0 + 16 j + r16 in the MFMA A layout,
+  // values (dims 2 lane, 2 lane + 1) of every token; rows past the block read
+  // the block's first token again and are masked
+  struct Blk {
+    uint4 ka[TB / 16][NKL];
+    uint2 vr[TB];
+  };
+  auto load_blk = [&](Blk& B, int64_t t0) {
     const int nt = (int)(t_hi - t0 < TB ? t_hi - t0 : TB);
-    // keys of tokens t0 + 16 j + r16 in the MFMA A layout; values: dims
-    // 2 lane, 2 lane + 1 of every token (rows past the block read the first
-    // token again and are masked)
-    uint4 ka[2][NKL];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < TB / 16; j++) {
       const int i = 16 * j + r16;
       const uint8_t* kp = Kb + (t0 + (i < nt ? i : 0)) * rs;
 #pragma unroll
       for (int s = 0; s < NKL; s++) {
         if constexpr (DT == WI_BF16)
-          ka[j][s] = *reinterpret_cast<const uint4*>(kp + (32 * s + 8 * kg) * 2);
+          B.ka[j][s] = *reinterpret_cast<const uint4*>(kp + (32 * s + 8 * kg) * 2);
         else
-          ka[j][s] = *reinterpret_cast<const uint4*>(kp + (32 * kg + 4 * s) * 4);
+          B.ka[j][s] = *reinterpret_cast<const uint4*>(kp + (32 * kg + 4 * s) * 4);
       }
     }
-    uint2 vr[TB];
 #pragma unroll
     for (int t = 0; t < TB; t++) {
       const uint8_t* vp = Vb + (t0 + (t < nt ? t : 0)) * rs;
       if constexpr (DT == WI_BF16)
-        vr[t].x = *reinterpret_cast<const uint32_t*>(vp + 4 * lane);
+        B.vr[t].x = *reinterpret_cast<const uint32_t*>(vp + 4 * lane);
       else
-        vr[t] = *reinterpret_cast<const uint2*>(vp + 8 * lane);
+        B.vr[t] = *reinterpret_cast<const uint2*>(vp + 8 * lane);
     }
+  };
+  auto compute_blk = [&](const Blk& B, int64_t t0) {
+    const int nt = (int)(t_hi - t0 < TB ? t_hi - t0 : TB);
     // logits z[token 16 j + 4 kg + jj][head r16]
-    float zt[2][4];
+    float zt[TB / 16][4];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < TB / 16; j++) {
       f32x4_t za = {0.f, 0.f, 0.f, 0.f};
       if constexpr (DT == WI_BF16) {
 #pragma unroll
         for (int s = 0; s < 4; s++)
-          za = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[j][s]),
+          za = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, B.ka[j][s]),
                                                        __builtin_bit_cast(bf16x8_t, bq[s]), za,
                                                        0, 0, 0);
       } else {
 #pragma unroll
         for (int s = 0; s < 8; s++) {
-          const uint32_t kx[4] = {ka[j][s].x, ka[j][s].y, ka[j][s].z, ka[j][s].w};
+          const uint32_t kx[4] = {B.ka[j][s].x, B.ka[j][s].y, B.ka[j][s].z, B.ka[j][s].w};
           const uint32_t qx[4] = {bq[s].x, bq[s].y, bq[s].z, bq[s].w};
 #pragma unroll
           for (int e = 0; e < 4; e++)
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(DN_THREADS) void dense_partial_kernel(
     // online softmax per head (column r16)
     float mx = m_run;
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < TB / 16; j++)
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) mx = fmaxf(mx, zt[j][jj]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(DN_THREADS) void dense_partial_kernel(
     m_run = mx;
     float ls = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < TB / 16; j++) {
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         const float p = zt[j][jj] == -INFINITY ? 0.f : ex<DT>(zt[j][jj] - mx);
@@ -172,11 +178,11 @@ __global__ __launch_bounds__(DN_THREADS) void dense_partial_kernel(
     for (int t = 0; t < TB; t++) {
       float v0, v1;
       if constexpr (DT == WI_BF16) {
-        v0 = __uint_as_float(vr[t].x << 16);
-        v1 = __uint_as_float(vr[t].x & 0xFFFF0000u);
+        v0 = __uint_as_float(B.vr[t].x << 16);
+        v1 = __uint_as_float(B.vr[t].x & 0xFFFF0000u);
       } else {
-        v0 = __uint_as_float(vr[t].x);
-        v1 = __uint_as_float(vr[t].y);
+        v0 = __uint_as_float(B.vr[t].x);
+        v1 = __uint_as_float(B.vr[t].y);
       }
       const float* pt = &pb[wv][t * GS];
 #pragma unroll
@@ -190,6 +196,24 @@ __global__ __launch_bounds__(DN_THREADS) void dense_partial_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // two register buffers, alternating: the next block's loads are issued
+  // before the current block is computed
+  const int64_t step = (int64_t)DN_WAVES * TB;
+  Blk A, B;
+  int64_t t0 = t_lo + (int64_t)wv * TB;
+  if (t0 < t_hi) load_blk(A, t0);
+#pragma unroll 1
+  while (t0 < t_hi) {
+    const int64_t t1 = t0 + step;
+    if (t1 < t_hi) load_blk(B, t1);
+    compute_blk(A, t0);
+    if (t1 >= t_hi) break;
+    const int64_t t2 = t1 + step;
+    if (t2 < t_hi) load_blk(A, t2);
+    compute_blk(B, t1);
+    t0 = t2;
   }
   // per-wave state: l summed over the four lanes of each head column
   float lt = l_run + __shfl_xor(l_run, 16, 64);
@@ -226,31 +250,63 @@ __global__ __launch_bounds__(DN_THREADS) void dense_partial_kernel(
   }
 }
 
-// One workgroup per (unit, head): merge the W chunk partials.
+// One workgroup per (unit, head): merge the W chunk partials. The maxima,
+// weights and denominators are formed over all chunks in parallel (weights
+// kept in LDS), then each half of the workgroup sums the weighted
+// accumulators of every other chunk for one output dimension per thread.
+constexpr int MG_THREADS = 256;
+constexpr int MAX_CHUNKS = 1024;
+
+__device__ __forceinline__ float block_reduce(float v, float* lds, bool is_max) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float y = __shfl_xor(v, o, 64);
+    v = is_max ? fmaxf(v, y) : v + y;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = lds[0];
+  for (int i = 1; i < MG_THREADS / 64; i++) r = is_max ? fmaxf(r, lds[i]) : r + lds[i];
+  return r;
+}
+
 template <int DT>
-__global__ __launch_bounds__(D) void dense_merge_kernel(const float* __restrict__ part, int W,
-                                                        int G, int H, int Hq,
-                                                        float* __restrict__ out) {
-  const int u = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+__global__ __launch_bounds__(MG_THREADS) void dense_merge_kernel(const float* __restrict__ part,
+                                                                 int W, int G, int H, int Hq,
+                                                                 float* __restrict__ out) {
+  const int u = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int b = u / H, h = u % H;
+  __shared__ float fw[MAX_CHUNKS];
+  __shared__ float red[MG_THREADS / 64];
+  __shared__ float half_acc[D];
   const float* pu = part + (int64_t)u * W * G * PART + g * PART;
   float M = -INFINITY;
-  for (int w = 0; w < W; w++) M = fmaxf(M, pu[(int64_t)w * G * PART]);
-  float s = 0.f, l = 0.f;
-  for (int w = 0; w < W; w++) {
+  for (int w = tid; w < W; w += MG_THREADS) M = fmaxf(M, pu[(int64_t)w * G * PART]);
+  M = block_reduce(M, red, true);
+  float l = 0.f;
+  for (int w = tid; w < W; w += MG_THREADS) {
     const float* p = pu + (int64_t)w * G * PART;
-    const float m = p[0];
-    const float f = m == -INFINITY ? 0.f : ex<DT>(m - M);
+    const float f = p[0] == -INFINITY ? 0.f : ex<DT>(p[0] - M);
+    fw[w] = f;
     l = fmaf(f, p[1], l);
-    s = fmaf(f, p[2 + t], s);
   }
-  out[((int64_t)b * Hq + (int64_t)h * G + g) * D + t] = s / l;
+  l = block_reduce(l, red, false);  // its barriers also publish fw
+  const int t = tid & (D - 1), hf = tid >> 7;
+  float s = 0.f;
+#pragma unroll 8
+  for (int w = hf; w < W; w += 2) s = fmaf(fw[w], pu[(int64_t)w * G * PART + 2 + t], s);
+  if (hf == 1) half_acc[t] = s;
+  __syncthreads();
+  if (hf == 0) out[((int64_t)b * Hq + (int64_t)h * G + g) * D + t] = (s + half_acc[t]) / l;
 }
 
 }  // namespace
 
+// About 1024 workgroups over the call (four per compute unit): enough waves
+// to keep HBM busy, few enough chunk partials for a short merge.
 int dense_chunks(int U, int64_t N) {
-  int64_t W = (2048 + U - 1) / U;
+  int64_t W = (1024 + U - 1) / U;
   const int64_t by_len = (N + 255) / 256;  // at least 256 tokens per chunk
   if (W > by_len) W = by_len;
   if (W > 1024) W = 1024;
@@ -277,14 +333,14 @@ hipError_t launch_dense(int dtype, int B, int H, int Hq, int G, int64_t N, int64
     if (GS == 4) WI_DN(WI_BF16, 4);
     else if (GS == 8) WI_DN(WI_BF16, 8);
     else WI_DN(WI_BF16, 16);
-    WI_LAUNCH(K_DENSE_MERGE, dense_merge_kernel<WI_BF16>, dim3(U, G), dim3(D), 0, s, part, W,
-              G, H, Hq, out);
+    WI_LAUNCH(K_DENSE_MERGE, dense_merge_kernel<WI_BF16>, dim3(U, G), dim3(MG_THREADS), 0, s,
+              part, W, G, H, Hq, out);
   } else {
     if (GS == 4) WI_DN(WI_F32, 4);
     else if (GS == 8) WI_DN(WI_F32, 8);
     else WI_DN(WI_F32, 16);
-    WI_LAUNCH(K_DENSE_MERGE, dense_merge_kernel<WI_F32>, dim3(U, G), dim3(D), 0, s, part, W,
-              G, H, Hq, out);
+    WI_LAUNCH(K_DENSE_MERGE, dense_merge_kernel<WI_F32>, dim3(U, G), dim3(MG_THREADS), 0, s,
+              part, W, G, H, Hq, out);
   }
 #undef WI_DN
   return hipGetLastError();
