@@ -317,6 +317,56 @@ wi_status wi_recall_at_k(const wi_index_desc *desc, const wi_decode_desc *ddesc,
                          int32_t *top_tokens, void *ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* ---- wave buffer: a GPU block cache in front of a host-memory tier -- */
+/* framerc blog section 2.2 (wave buffer): the KV blocks live in CPU
+ * memory; a GPU cache holds hot 2 KB blocks with a block -> slot mapping
+ * table. The synchronous access path reads a retrieved block from its cache
+ * slot when cached and from CPU memory otherwise; the asynchronous update
+ * path keeps an LRU replacement and the table. Per unit:
+ *   block_slot  device [U][block_cap] int32   cache slot of a block, or -1
+ *   slot_block  device [U][n_slots] int32     block held by a slot, or -1
+ *   slot_last   device [U][n_slots] uint32    last step that used the slot
+ *                                             (0: never)
+ *   cache_k/v   device [U][n_slots * T][128] dtype   the cached blocks
+ * The caller owns every buffer; wi_wave_buffer_reset empties the tables. */
+typedef struct {
+  int32_t n_slots;          /* cache capacity per unit in blocks, 1 .. 8192 */
+  int32_t *block_slot;
+  int32_t *slot_block;
+  uint32_t *slot_last;
+  void *cache_k;
+  void *cache_v;
+} wi_wave_buffer;
+
+/* Empty the cache tables (every block uncached, every slot free). */
+wi_status wi_wave_buffer_reset(const wi_index_desc *desc, const wi_wave_buffer *wb,
+                               hipStream_t stream);
+
+/* Host-only: workspace bytes of wi_decode_attention_wb. */
+wi_status wi_decode_wb_sizes(const wi_index_desc *desc,
+                             const wi_decode_desc *ddesc, int32_t n_slots,
+                             size_t *workspace_bytes);
+
+/* wi_decode_attention with the KV blocks in host memory behind the wave
+ * buffer. bufs->k_blocks and bufs->v_blocks are pinned host memory
+ * (hipHostMalloc or equivalent, device-visible) holding the index's block
+ * pools; every other index buffer is device memory. The output equals
+ * wi_decode_attention's on the same index bit for bit: a retrieved row is
+ * read from its block's cache slot when the block is cached and from host
+ * memory otherwise. Then the update path runs for step `step` (> 0, larger
+ * than every earlier step of this wave buffer): the blocks of the retrieved
+ * clusters, ascending, are looked up; hits mark their slot used at `step`;
+ * misses, ascending, take the slots not used at `step` in order of (last
+ * use, slot id), evicting those slots' blocks, and are copied from host
+ * memory into them (as many misses as there are such slots).
+ *   stats   device [U][2] int32 (hits, misses) of this step, or NULL */
+wi_status wi_decode_attention_wb(const wi_index_desc *desc,
+                                 const wi_decode_desc *ddesc,
+                                 const wi_index_bufs *bufs,
+                                 const wi_wave_buffer *wb, uint32_t step,
+                                 const void *q, float *out, int32_t *stats,
+                                 void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Largest decode workspace that wi_decode_attention_noalloc serves: 16 MiB
  * (the five model shapes of this library need at most 11.5 MiB: 8 units of
  * 65536 clusters, or 64 units of 8192). */

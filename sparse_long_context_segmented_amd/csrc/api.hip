@@ -270,7 +270,7 @@ thread_local int t_cur = -1;
 const char* const kNames[wi::K_COUNT] = {
     "zero", "copy_init", "kpp_init", "kpp_weights", "kpp_round", "assign", "assign_fix",
     "sort_update", "seg_scan", "layout", "score", "select_attend", "rank", "exec", "append",
-    "merge", "dense", "dense_merge", "recall"};
+    "merge", "dense", "dense_merge", "recall", "wb_update", "wb_fill"};
 
 hipEvent_t take_event() {
   if (!t_pool.empty()) {
@@ -728,6 +728,145 @@ wi_status wi_dense_attention(const wi_index_desc* desc, const wi_decode_desc* dd
   CHECK_HIP(wi::launch_dense(ds.dtype, ds.B, ds.H, ds.Hq, ds.G, ds.N, ds.sb, ds.sh, ds.st,
                              ds.scale, k, v, q, out, reinterpret_cast<float*>(ws), stream),
             "dense attention");
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device-visible address of a host-memory range of `bytes` bytes (pinned,
+// mapped): both ends must resolve to host memory of one mapping.
+wi_status host_range(const void* p, int64_t bytes, const char* name, const void** dev) {
+  if (!p) return fail(WI_E_INVALID, "%s is NULL", name);
+  if (!aligned16(p)) return fail(WI_E_INVALID, "%s is not 16-byte aligned", name);
+  hipPointerAttribute_t a0, a1;
+  if (hipPointerGetAttributes(&a0, p) != hipSuccess || a0.type != hipMemoryTypeHost ||
+      !a0.devicePointer) {
+    (void)hipGetLastError();
+    return fail(WI_E_INVALID, "%s is not pinned host memory visible to the device", name);
+  }
+  const void* end = reinterpret_cast<const uint8_t*>(p) + (bytes - 1);
+  if (hipPointerGetAttributes(&a1, end) != hipSuccess || a1.type != hipMemoryTypeHost ||
+      reinterpret_cast<const uint8_t*>(a1.devicePointer) -
+              reinterpret_cast<const uint8_t*>(a0.devicePointer) != bytes - 1) {
+    (void)hipGetLastError();
+    return fail(WI_E_INVALID, "%s: the pinned host allocation is smaller than the block pool",
+                name);
+  }
+  *dev = a0.devicePointer;
+  return WI_OK;
+}
+
+// Decode workspace, then the update path's lists: needed/missed blocks
+// [U][2 cap], admitted (block, slot) pairs [U][2 S], counts [U][4].
+int64_t wb_ws_bytes(const wi::Geom& g, const DecodeShape& ds, int S) {
+  return carve_decode(g, ds, nullptr, nullptr) + align256((int64_t)g.U * 2 * g.cap * 4) +
+         align256((int64_t)g.U * 2 * S * 4) + align256((int64_t)g.U * 4 * 4);
+}
+
+wi_status check_wb(const wi::Geom& g, const wi_wave_buffer* wb) {
+  if (!wb) return fail(WI_E_INVALID, "wave buffer is NULL");
+  if (wb->n_slots < 1 || wb->n_slots > wi::wb_max_slots())
+    return fail(WI_E_INVALID, "n_slots %d outside [1, %d]", wb->n_slots, wi::wb_max_slots());
+  CHECK_PTR(wb->block_slot, "wb->block_slot");
+  CHECK_PTR(wb->slot_block, "wb->slot_block");
+  CHECK_PTR(wb->slot_last, "wb->slot_last");
+  CHECK_PTR(wb->cache_k, "wb->cache_k");
+  CHECK_PTR(wb->cache_v, "wb->cache_v");
+  (void)g;
+  return WI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+wi_status wi_wave_buffer_reset(const wi_index_desc* desc, const wi_wave_buffer* wb,
+                               hipStream_t stream) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  st = check_wb(g, wb);
+  if (st != WI_OK) return st;
+  wi::WaveBufArgs w{wb->n_slots, wb->block_slot, wb->slot_block, wb->slot_last,
+                    wb->cache_k, wb->cache_v, nullptr, nullptr};
+  CHECK_HIP(wi::launch_wb_reset(g, w, stream), "wave buffer reset");
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_decode_wb_sizes(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                             int32_t n_slots, size_t* workspace_bytes) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  DecodeShape ds;
+  st = make_decode(g, ddesc, &ds);
+  if (st != WI_OK) return st;
+  if (n_slots < 1 || n_slots > wi::wb_max_slots())
+    return fail(WI_E_INVALID, "n_slots %d outside [1, %d]", n_slots, wi::wb_max_slots());
+  if (workspace_bytes) *workspace_bytes = (size_t)wb_ws_bytes(g, ds, n_slots);
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_decode_attention_wb(const wi_index_desc* desc, const wi_decode_desc* ddesc,
+                                 const wi_index_bufs* bufs, const wi_wave_buffer* wb,
+                                 uint32_t step, const void* q, float* out, int32_t* stats,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  DecodeShape ds;
+  st = make_decode(g, ddesc, &ds);
+  if (st != WI_OK) return st;
+  st = check_wb(g, wb);
+  if (st != WI_OK) return st;
+  if (step == 0) return fail(WI_E_INVALID, "step must be > 0");
+  if (!bufs) return fail(WI_E_INVALID, "bufs is NULL");
+  CHECK_PTR(bufs->centroids, "bufs->centroids");
+  CHECK_PTR(bufs->cluster_size, "bufs->cluster_size");
+  CHECK_PTR(bufs->value_sum, "bufs->value_sum");
+  CHECK_PTR(bufs->block_off, "bufs->block_off");
+  if (g.n_st > 0) {
+    CHECK_PTR(bufs->steady_k, "bufs->steady_k");
+    CHECK_PTR(bufs->steady_v, "bufs->steady_v");
+  }
+  if (g.n_pend > 0) {
+    CHECK_PTR(bufs->pend_k, "bufs->pend_k");
+    CHECK_PTR(bufs->pend_v, "bufs->pend_v");
+  }
+  CHECK_PTR(q, "q");
+  CHECK_PTR(out, "out");
+  if (stats && !aligned16(stats)) return fail(WI_E_INVALID, "stats is not 16-byte aligned");
+  const int64_t pool = (int64_t)g.U * g.cap * g.T * wi::D * (g.dtype == WI_BF16 ? 2 : 4);
+  const void *hk = nullptr, *hv = nullptr;
+  st = host_range(bufs->k_blocks, pool, "bufs->k_blocks", &hk);
+  if (st != WI_OK) return st;
+  st = host_range(bufs->v_blocks, pool, "bufs->v_blocks", &hv);
+  if (st != WI_OK) return st;
+  const int64_t need = wb_ws_bytes(g, ds, wb->n_slots);
+  if (!ws || (int64_t)ws_bytes < need)
+    return fail(WI_E_WORKSPACE, "workspace %zu bytes < %lld required", ws_bytes, (long long)need);
+  if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  wi::DecodeWs w;
+  int64_t off = carve_decode(g, ds, base, &w);
+  int32_t* lists = reinterpret_cast<int32_t*>(base + off);
+  off += align256((int64_t)g.U * 2 * g.cap * 4);
+  int32_t* fill = reinterpret_cast<int32_t*>(base + off);
+  off += align256((int64_t)g.U * 2 * wb->n_slots * 4);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + off);
+  wi::WaveBufArgs wa{wb->n_slots, wb->block_slot, wb->slot_block, wb->slot_last,
+                     wb->cache_k, wb->cache_v, hk, hv};
+  wi::DecodeArgs a{&g, ds.Hq, ds.G, ds.GS, ds.K_r, ds.K_e, ds.W, ds.scale};
+  CHECK_HIP(wi::launch_score(a, bufs->centroids, q, w, stream), "score");
+  CHECK_HIP(wi::launch_fused(a, *bufs, q, out, w, true, stream, &wa), "select/attend");
+  CHECK_HIP(wi::launch_wb_update(g, wa, bufs->cluster_size, bufs->block_off, w.zone, step,
+                                 lists, fill, counts, stats, stream),
+            "wave buffer update");
   g_err[0] = 0;
   return WI_OK;
 }

@@ -96,6 +96,13 @@ struct FusedArgs {
   uint8_t* zone;           // nullable: [U][C] 1 = retrieval, 2 = estimation
   const void* pk;          // nullable while n_pend = 0: [U][seg_len] pending rows
   const void* pv;
+  // wave buffer (cached kernel only): kblk/vblk are then the host tier's
+  // blocks; a block with b2s[u][blk] = s >= 0 is read from cache slot s
+  const int32_t* b2s;      // [U][nblk]
+  const void* ck;          // [U][nslot * T] rows
+  const void* cv;
+  int64_t nblk;
+  int nslot;
   int C, Cp, n_st, n_pend, seg_len, G, H, Hq, K_r, K_e, W, lgT, NB;
   int64_t capT;
   float scale;
@@ -214,7 +221,7 @@ struct Lds {
 // Kept a separate instantiation so that the common kernel holds no
 // re-staging loads, after which the compiler would place waits for
 // outstanding loads.
-template <int DT, int GS, bool BIG>
+template <int DT, int GS, bool BIG, bool CACHED>
 __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   using L = Lds<GS>;
   constexpr int NTILE = DT == WI_BF16 ? 2 : 1;  // 16-token MFMA tiles per wave block
@@ -458,6 +465,19 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   auto xrow = [&](const uint8_t* st8, const uint8_t* p8, int x) {
     return x < n_st ? st8 + (int64_t)x * RB : p8 + (int64_t)(x - n_st) * RB;
   };
+  // row `row` of the unit's blocks: from its cache slot sl when the block is
+  // cached, else from the block pool (HBM, or the host tier when CACHED)
+  const uint8_t* ck8 = CACHED ? reinterpret_cast<const uint8_t*>(a.ck) +
+                                    (int64_t)u * a.nslot * (RB << a.lgT) : nullptr;
+  const uint8_t* cv8 = CACHED ? reinterpret_cast<const uint8_t*>(a.cv) +
+                                    (int64_t)u * a.nslot * (RB << a.lgT) : nullptr;
+  auto brow = [&](const uint8_t* pool8, const uint8_t* cache8, int row, int sl) {
+    if constexpr (CACHED) {
+      if (sl >= 0 && sl < a.nslot)
+        return cache8 + (((int64_t)sl << a.lgT) + (row & ((1 << a.lgT) - 1))) * RB;
+    }
+    return pool8 + (int64_t)row * RB;
+  };
   // a valid row of at least RB bytes, read by lanes without an item
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.vsum + uC * D);
   const int lgT = a.lgT;
@@ -477,7 +497,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     }
     // up to 4 retrieval candidates per wave; lanes 0-31 read the key rows,
     // 32-63 the value rows, one 128-byte line each
-    uint64_t cand = __ballot(maybeR);
+    uint64_t cand = CACHED ? 0ull : __ballot(maybeR);
 #pragma unroll
     for (int c = 0; c < 4; c++) {
       if (cand) {
@@ -749,6 +769,16 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
         rowj[j] = item < nS ? s_lo + item
                             : (item < nT ? (Rblk[pos] << lgT) + (t - Rtok[pos]) : 0);
       }
+      // cache slot of each retrieved row's block (-1: not cached)
+      int slj[NTILE];
+#pragma unroll
+      for (int j = 0; j < NTILE; j++) {
+        slj[j] = -1;
+        if constexpr (CACHED) {
+          const int item = t0 + 16 * j + r16;
+          if (item >= nS && item < nT) slj[j] = a.b2s[(int64_t)u * a.nblk + (rowj[j] >> lgT)];
+        }
+      }
       // (b) loads: keys in the MFMA layout, two value dims per lane of every
       // token, the estimation clusters' value sums. Tiles and groups of rows
       // with no item issue no loads (ntw and new_ are uniform over the wave):
@@ -759,7 +789,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
         if (16 * j < ntw) {
           const int item = t0 + 16 * j + r16;
           const uint8_t* kp =
-              item < nT ? (item < nS ? xrow(sk8, pk8, rowj[j]) : kb8 + (int64_t)rowj[j] * RB)
+              item < nT ? (item < nS ? xrow(sk8, pk8, rowj[j]) : brow(kb8, ck8, rowj[j], slj[j]))
                         : dummy;
 #pragma unroll
           for (int s = 0; s < NKL; s++) {
@@ -780,8 +810,9 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
 #pragma unroll
           for (int t = t8; t < t8 + 8; t++) {
             const int row = rdl(rowj[t / 16], t % 16);
+            const int sl = CACHED ? rdl(slj[t / 16], t % 16) : -1;
             const uint8_t* vpt =
-                t < ntw ? (t0 + t < nS ? xrow(sv8, pv8, row) : vb8 + (int64_t)row * RB) : dummy;
+                t < ntw ? (t0 + t < nS ? xrow(sv8, pv8, row) : brow(vb8, cv8, row, sl)) : dummy;
             if constexpr (DT == WI_BF16)
               vr[t].x = *reinterpret_cast<const uint32_t*>(vpt + 4 * lane);
             else
@@ -1058,24 +1089,29 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   else combine(std::integral_constant<int, MAX_WG>{});
 }
 
-template <int DT, bool BIG>
+template <int DT, bool BIG, bool CACHED>
 hipError_t launch_fused_big(const DecodeArgs& da, const FusedArgs& fa, hipStream_t s) {
   dim3 grid(da.W, da.g->U);
-  if (da.GS == 4) WI_LAUNCH(K_FUSED, (fused_kernel<DT, 4, BIG>), grid, dim3(NT), 0, s, fa);
-  else if (da.GS == 8) WI_LAUNCH(K_FUSED, (fused_kernel<DT, 8, BIG>), grid, dim3(NT), 0, s, fa);
-  else WI_LAUNCH(K_FUSED, (fused_kernel<DT, 16, BIG>), grid, dim3(NT), 0, s, fa);
+  if (da.GS == 4)
+    WI_LAUNCH(K_FUSED, (fused_kernel<DT, 4, BIG, CACHED>), grid, dim3(NT), 0, s, fa);
+  else if (da.GS == 8)
+    WI_LAUNCH(K_FUSED, (fused_kernel<DT, 8, BIG, CACHED>), grid, dim3(NT), 0, s, fa);
+  else
+    WI_LAUNCH(K_FUSED, (fused_kernel<DT, 16, BIG, CACHED>), grid, dim3(NT), 0, s, fa);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool CACHED>
 hipError_t launch_fused_dt(const DecodeArgs& da, const FusedArgs& fa, hipStream_t s) {
-  return fa.C > CL ? launch_fused_big<DT, true>(da, fa, s) : launch_fused_big<DT, false>(da, fa, s);
+  return fa.C > CL ? launch_fused_big<DT, true, CACHED>(da, fa, s)
+                   : launch_fused_big<DT, false, CACHED>(da, fa, s);
 }
 
 }  // namespace
 
 hipError_t launch_fused(const DecodeArgs& da, const wi_index_bufs& bf, const void* q,
-                        float* out, const DecodeWs& ws, bool want_lists, hipStream_t s) {
+                        float* out, const DecodeWs& ws, bool want_lists, hipStream_t s,
+                        const WaveBufArgs* wb) {
   const Geom& g = *da.g;
   FusedArgs fa;
   fa.key = ws.key;
@@ -1110,8 +1146,20 @@ hipError_t launch_fused(const DecodeArgs& da, const wi_index_bufs& bf, const voi
   fa.lgT = g.T == 8 ? 3 : 2;
   fa.capT = g.cap * g.T;
   fa.scale = da.scale;
-  return g.dtype == WI_BF16 ? launch_fused_dt<WI_BF16>(da, fa, s)
-                            : launch_fused_dt<WI_F32>(da, fa, s);
+  fa.b2s = wb ? wb->block_slot : nullptr;
+  fa.ck = wb ? wb->cache_k : nullptr;
+  fa.cv = wb ? wb->cache_v : nullptr;
+  fa.nblk = g.cap;
+  fa.nslot = wb ? wb->n_slots : 0;
+  if (wb) {
+    // the blocks are read from the host tier (device-visible addresses)
+    fa.kblk = wb->host_k;
+    fa.vblk = wb->host_v;
+    return g.dtype == WI_BF16 ? launch_fused_dt<WI_BF16, true>(da, fa, s)
+                              : launch_fused_dt<WI_F32, true>(da, fa, s);
+  }
+  return g.dtype == WI_BF16 ? launch_fused_dt<WI_BF16, false>(da, fa, s)
+                            : launch_fused_dt<WI_F32, false>(da, fa, s);
 }
 
 }  // namespace wi

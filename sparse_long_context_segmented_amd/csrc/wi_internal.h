@@ -191,7 +191,7 @@ __device__ __forceinline__ float wave_max(float v) {
 enum KernelId {
   K_ZERO, K_COPY, K_KPP_INIT, K_KPP_WEIGHTS, K_KPP_ROUND, K_ASSIGN, K_ASSIGN_FIX,
   K_SORT_UPDATE, K_SEG_SCAN, K_LAYOUT, K_SCORE, K_FUSED, K_RANK,
-  K_EXEC, K_APPEND, K_MERGE, K_DENSE, K_DENSE_MERGE, K_RECALL, K_COUNT
+  K_EXEC, K_APPEND, K_MERGE, K_DENSE, K_DENSE_MERGE, K_RECALL, K_WB_UPDATE, K_WB_FILL, K_COUNT
 };
 void tmark_begin(KernelId id, hipStream_t s);
 void tmark_end(hipStream_t s);
@@ -231,8 +231,29 @@ struct DecodeArgs {
 int score_blocks(const Geom& g);  // score-kernel workgroups per unit
 hipError_t launch_score(const DecodeArgs& a, const void* centroids, const void* q,
                         const DecodeWs& ws, hipStream_t s);
+// The wave buffer of one decode call: the GPU block cache and its tables,
+// and the host tier's block pools as device-visible addresses.
+struct WaveBufArgs {
+  int n_slots;
+  int32_t* block_slot;   // [U][cap]
+  int32_t* slot_block;   // [U][n_slots]
+  uint32_t* slot_last;   // [U][n_slots]
+  void* cache_k;         // [U][n_slots * T][128]
+  void* cache_v;
+  const void* host_k;    // [U][cap * T][128] in host memory
+  const void* host_v;
+};
 hipError_t launch_fused(const DecodeArgs& a, const wi_index_bufs& b, const void* q,
-                        float* out, const DecodeWs& ws, bool want_lists, hipStream_t s);
+                        float* out, const DecodeWs& ws, bool want_lists, hipStream_t s,
+                        const WaveBufArgs* wb = nullptr);
+// Wave-buffer maintenance: empty tables; the per-step update from the
+// retrieval zones (zone flags) and the fill of the admitted blocks.
+int wb_max_slots();
+hipError_t launch_wb_reset(const Geom& g, const WaveBufArgs& wb, hipStream_t s);
+hipError_t launch_wb_update(const Geom& g, const WaveBufArgs& wb, const int32_t* cluster_size,
+                            const int32_t* block_off, const uint8_t* zone, uint32_t step,
+                            int32_t* need, int32_t* fill, int32_t* counts, int32_t* stats,
+                            hipStream_t s);
 hipError_t launch_append(const Geom& g, const wi_index_bufs& b, const void* k_new,
                          const void* v_new, hipStream_t s);
 // The grown index nw (geometry gn) from the old index o (geometry go) and the

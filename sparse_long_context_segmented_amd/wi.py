@@ -24,7 +24,8 @@ STATUS = {0: "WI_OK", 1: "WI_E_INVALID", 2: "WI_E_UNSUPPORTED", 3: "WI_E_WORKSPA
 EXPORTS = ("wi_index_sizes", "wi_build_index", "wi_decode_sizes", "wi_decode_attention",
            "wi_decode_attention_noalloc", "wi_append_token", "wi_extend_sizes",
            "wi_extend_index", "wi_layer_plan", "wi_dense_sizes", "wi_dense_attention",
-           "wi_recall_sizes", "wi_recall_at_k", "wi_status_str", "wi_last_error",
+           "wi_recall_sizes", "wi_recall_at_k", "wi_wave_buffer_reset", "wi_decode_wb_sizes",
+           "wi_decode_attention_wb", "wi_status_str", "wi_last_error",
            "wi_timing_start", "wi_timing_stop", "wi_kernel_name")
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -50,6 +51,12 @@ class IndexBufs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "centroids", "cluster_size", "value_sum", "block_off", "k_blocks", "v_blocks",
         "slot_token", "steady_k", "steady_v", "assign", "pend_k", "pend_v")]
+
+
+class WaveBufferDesc(ctypes.Structure):
+    _fields_ = [("n_slots", ctypes.c_int32), ("block_slot", ctypes.c_void_p),
+                ("slot_block", ctypes.c_void_p), ("slot_last", ctypes.c_void_p),
+                ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p)]
 
 
 class DecodeDesc(ctypes.Structure):
@@ -98,6 +105,13 @@ def lib():
         L.wi_recall_sizes.restype = ctypes.c_int
         L.wi_recall_at_k.argtypes = [P, P, P, P, P, i32, i32, i32, P, P, P, ctypes.c_size_t, P]
         L.wi_recall_at_k.restype = ctypes.c_int
+        L.wi_wave_buffer_reset.argtypes = [P, P, P]
+        L.wi_wave_buffer_reset.restype = ctypes.c_int
+        L.wi_decode_wb_sizes.argtypes = [P, P, i32, P]
+        L.wi_decode_wb_sizes.restype = ctypes.c_int
+        L.wi_decode_attention_wb.argtypes = [P, P, P, P, ctypes.c_uint32, P, P, P, P,
+                                             ctypes.c_size_t, P]
+        L.wi_decode_attention_wb.restype = ctypes.c_int
         L.wi_status_str.argtypes = [ctypes.c_int]
         L.wi_status_str.restype = ctypes.c_char_p
         L.wi_last_error.argtypes = []
@@ -364,6 +378,75 @@ def recall_at_k(index: Index, ddesc: DecodeDesc, q: torch.Tensor, sel_ids: torch
                                 _ptr(q), _ptr(sel_ids), sel_ids.shape[-1], n_r, k, _ptr(rec),
                                 _ptr(top), _ptr(ws), ws.numel(), _stream(stream)))
     return (rec, top) if want_top else rec
+
+
+@dataclass
+class WaveBuffer:
+    """GPU block cache and tables of the wave buffer (device tensors)."""
+    n_slots: int
+    block_slot: torch.Tensor   # [U, cap] int32
+    slot_block: torch.Tensor   # [U, n_slots] int32
+    slot_last: torch.Tensor    # [U, n_slots] int32 (uint32 values)
+    cache_k: torch.Tensor      # [U, n_slots * T, 128]
+    cache_v: torch.Tensor
+
+    def desc(self) -> WaveBufferDesc:
+        return WaveBufferDesc(self.n_slots, *[_ptr(t) for t in (
+            self.block_slot, self.slot_block, self.slot_last, self.cache_k, self.cache_v)])
+
+
+def alloc_wave_buffer(desc: IndexDesc, n_slots: int, device="cuda", stream=None) -> WaveBuffer:
+    """Allocate a wave buffer of n_slots blocks per unit and empty it."""
+    ns, C, cap, _ = index_sizes(desc)
+    U = desc.batch * desc.n_kv_heads
+    T = 2048 // (128 * (4 if desc.dtype == WI_F32 else 2))
+    dt = torch_dtype(desc)
+    wb = WaveBuffer(n_slots, torch.empty(U, cap, dtype=torch.int32, device=device),
+                    torch.empty(U, n_slots, dtype=torch.int32, device=device),
+                    torch.empty(U, n_slots, dtype=torch.int32, device=device),
+                    torch.empty(U, n_slots * T, 128, dtype=dt, device=device),
+                    torch.empty(U, n_slots * T, 128, dtype=dt, device=device))
+    wd = wb.desc()
+    _check(lib().wi_wave_buffer_reset(ctypes.byref(desc), ctypes.byref(wd), _stream(stream)))
+    return wb
+
+
+def host_tier(index: Index) -> Index:
+    """The same index with its K/V block pools moved to pinned host memory."""
+    hk = torch.empty(index.k_blocks.shape, dtype=index.k_blocks.dtype, pin_memory=True)
+    hv = torch.empty(index.v_blocks.shape, dtype=index.v_blocks.dtype, pin_memory=True)
+    hk.copy_(index.k_blocks)
+    hv.copy_(index.v_blocks)
+    return Index(index.desc, index.centroids, index.cluster_size, index.value_sum,
+                 index.block_off, hk, hv, index.slot_token, index.steady_k, index.steady_v,
+                 index.assign, index.pend_k, index.pend_v)
+
+
+def decode_wb_sizes(desc: IndexDesc, ddesc: DecodeDesc, n_slots: int) -> int:
+    ws = ctypes.c_size_t()
+    _check(lib().wi_decode_wb_sizes(ctypes.byref(desc), ctypes.byref(ddesc), n_slots,
+                                    ctypes.byref(ws)))
+    return ws.value
+
+
+def decode_attention_wb(index: Index, ddesc: DecodeDesc, wb: WaveBuffer, step: int,
+                        q: torch.Tensor, out: torch.Tensor | None = None,
+                        stats: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Run wi_decode_attention_wb (index from host_tier); returns out."""
+    desc = index.desc
+    wsb = decode_wb_sizes(desc, ddesc, wb.n_slots)
+    if out is None:
+        out = torch.empty(desc.batch, ddesc.n_q_heads, 128, dtype=torch.float32, device=q.device)
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    bufs = index.bufs()
+    wd = wb.desc()
+    _check(lib().wi_decode_attention_wb(ctypes.byref(desc), ctypes.byref(ddesc),
+                                        ctypes.byref(bufs), ctypes.byref(wd), step, _ptr(q),
+                                        _ptr(out), _ptr(stats), _ptr(ws), ws.numel(),
+                                        _stream(stream)))
+    return out
 
 
 def timing_start():
