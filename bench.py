@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle's timed decode loop")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-wb", action="store_true", help="skip the wave-buffer leg")
     ap.add_argument("--wg", type=int, default=0,
                     help="fused-kernel workgroups per (sequence, KV head); 0 = automatic")
     ap.add_argument("--profile", action="store_true",
@@ -277,6 +278,10 @@ def main():
                 "kernel_ms": {k: round(v, 5) for k, v in avg.items()},
                 "algorithmic_bytes": {k: int(v) for k, v in per_kernel.items()}}
 
+    # ---- wave buffer: the same index with its K/V blocks in pinned host
+    # memory behind a GPU block cache, on a drifting query stream ----
+    wave = wave_buffer_leg(w, desc, ix, dd, qt, q, a.steps, a.warmup) if not a.no_wb else None
+
     qps = w.batch * a.steps / (step_ms * a.steps * 1e-3)
     res = {
         "metric": "decode attention queries/s per layer at 128K ctx; achieved HBM GB/s vs peak",
@@ -296,6 +301,7 @@ def main():
         "roofline": roofline,
         "build": build,
         "policy": policy,
+        "wave_buffer": wave,
         "gen_s": round(gen_s, 1),
     }
 
@@ -442,6 +448,79 @@ def model_bench(a, w):
                                            queries_per_step=w.batch * L)
         del host0
     print(json.dumps(res), flush=True)
+
+
+def wave_buffer_leg(w, desc, ix, dd, qt, q, steps, warmup, fracs=(0.05, 0.10, 0.20)):
+    """Decode through the wave buffer (K/V blocks in pinned host memory, a GPU
+    cache of a fraction of the used blocks per unit) on a seeded drifting
+    query stream: hit rate, misses per step and the step time, beside the
+    HBM-resident decode of the same queries."""
+    import torch
+    from sparse_long_context_segmented_amd import synth, wi
+    dev = qt.device
+    stream = torch.cuda.current_stream()
+    rng = np.random.default_rng(1234)
+    cur, qs = q.copy(), []
+    for _ in range(warmup + steps):
+        cur = cur + 0.35 * rng.standard_normal(q.shape).astype(np.float32)
+        qs.append(torch.from_numpy(synth._round_to_dtype(0.8 * cur + 0.2 * q, w.dtype))
+                  .to(dev, qt.dtype))
+    hix = wi.host_tier(ix)
+    U = w.batch * w.n_kv_heads
+    used = int(ix.block_off[:, -1].max())
+    e = 2 if w.dtype == "bf16" else 4
+    T = 2048 // (128 * e)
+    out = torch.empty(w.batch, w.n_q_heads, 128, dtype=torch.float32, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the HBM-resident decode of the same stream
+    wsd = torch.empty(wi.decode_sizes(desc, dd), dtype=torch.uint8, device=dev)
+    for i in range(warmup):
+        wi.decode_attention(ix, dd, qs[i], out=out, ws=wsd)
+    ev0.record(stream)
+    for i in range(warmup, warmup + steps):
+        wi.decode_attention(ix, dd, qs[i], out=out, ws=wsd)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    res = {"queries": "seeded random walk of the workload's queries (step 0.35, pulled 20 % "
+                      "back to the start)",
+           "hbm_ms_per_step": round(ev0.elapsed_time(ev1) / steps, 5), "caches": []}
+    for frac in fracs:
+        S = max(1, min(8192, int(frac * used)))
+        wb = wi.alloc_wave_buffer(desc, S, dev)
+        ws = torch.empty(wi.decode_wb_sizes(desc, dd, S), dtype=torch.uint8, device=dev)
+        stats = torch.zeros(warmup + steps, U, 2, dtype=torch.int32, device=dev)
+        for i in range(warmup):
+            wi.decode_attention_wb(hix, dd, wb, i + 1, qs[i], out=out, stats=stats[i], ws=ws)
+        ev0.record(stream)
+        for i in range(warmup, warmup + steps):
+            wi.decode_attention_wb(hix, dd, wb, i + 1, qs[i], out=out, stats=stats[i], ws=ws)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        st = stats[warmup:].cpu().numpy().astype(np.int64)
+        hits, misses = int(st[:, :, 0].sum()), int(st[:, :, 1].sum())
+        # kernel durations of the same steps replayed on a second cache (the
+        # timing hook's events would perturb the timed loop above)
+        wb2 = wi.alloc_wave_buffer(desc, S, dev)
+        for i in range(warmup):
+            wi.decode_attention_wb(hix, dd, wb2, i + 1, qs[i], out=out, ws=ws)
+        wi.timing_start()
+        for i in range(warmup, warmup + steps):
+            wi.decode_attention_wb(hix, dd, wb2, i + 1, qs[i], out=out, ws=ws)
+        kk = {}
+        for name, ms in wi.timing_stop():
+            kk.setdefault(name, []).append(ms)
+        del wb2
+        res["caches"].append({
+            "slots_per_unit": S, "fraction_of_blocks": round(S / used, 4),
+            "cache_MB": round(2 * U * S * T * 128 * e / 1e6, 1),
+            "hit_rate": round(hits / max(1, hits + misses), 4),
+            "misses_per_step": round(misses / steps, 1),
+            "host_read_MB_per_step": round(misses / steps * 2 * 2 * T * 128 * e / 1e6, 3),
+            "ms_per_step": round(ev0.elapsed_time(ev1) / steps, 5),
+            "kernel_ms": {k: round(float(np.mean(v)), 5) for k, v in kk.items()}})
+        del wb, ws
+    del hix
+    return res
 
 
 def cpu_baseline(w, K, V, q, k_r, k_e, seconds, units, layer=0, units_per_step=None,

@@ -327,6 +327,8 @@ wi_status wi_recall_at_k(const wi_index_desc *desc, const wi_decode_desc *ddesc,
  *   slot_block  device [U][n_slots] int32     block held by a slot, or -1
  *   slot_last   device [U][n_slots] uint32    last step that used the slot
  *                                             (0: never)
+ *   slot_order  device [U][n_slots] int32     the slots sorted by (slot_last,
+ *                                             slot id): the eviction order
  *   cache_k/v   device [U][n_slots * T][128] dtype   the cached blocks
  * The caller owns every buffer; wi_wave_buffer_reset empties the tables. */
 typedef struct {
@@ -336,6 +338,7 @@ typedef struct {
   uint32_t *slot_last;
   void *cache_k;
   void *cache_v;
+  int32_t *slot_order;
 } wi_wave_buffer;
 
 /* Empty the cache tables (every block uncached, every slot free). */

@@ -773,6 +773,7 @@ wi_status check_wb(const wi::Geom& g, const wi_wave_buffer* wb) {
   CHECK_PTR(wb->block_slot, "wb->block_slot");
   CHECK_PTR(wb->slot_block, "wb->slot_block");
   CHECK_PTR(wb->slot_last, "wb->slot_last");
+  CHECK_PTR(wb->slot_order, "wb->slot_order");
   CHECK_PTR(wb->cache_k, "wb->cache_k");
   CHECK_PTR(wb->cache_v, "wb->cache_v");
   (void)g;
@@ -791,7 +792,7 @@ wi_status wi_wave_buffer_reset(const wi_index_desc* desc, const wi_wave_buffer* 
   st = check_wb(g, wb);
   if (st != WI_OK) return st;
   wi::WaveBufArgs w{wb->n_slots, wb->block_slot, wb->slot_block, wb->slot_last,
-                    wb->cache_k, wb->cache_v, nullptr, nullptr};
+                    wb->slot_order, wb->cache_k, wb->cache_v, nullptr, nullptr};
   CHECK_HIP(wi::launch_wb_reset(g, w, stream), "wave buffer reset");
   g_err[0] = 0;
   return WI_OK;
@@ -860,7 +861,7 @@ wi_status wi_decode_attention_wb(const wi_index_desc* desc, const wi_decode_desc
   off += align256((int64_t)g.U * 2 * wb->n_slots * 4);
   int32_t* counts = reinterpret_cast<int32_t*>(base + off);
   wi::WaveBufArgs wa{wb->n_slots, wb->block_slot, wb->slot_block, wb->slot_last,
-                     wb->cache_k, wb->cache_v, hk, hv};
+                     wb->slot_order, wb->cache_k, wb->cache_v, hk, hv};
   wi::DecodeArgs a{&g, ds.Hq, ds.G, ds.GS, ds.K_r, ds.K_e, ds.W, ds.scale};
   CHECK_HIP(wi::launch_score(a, bufs->centroids, q, w, stream), "score");
   CHECK_HIP(wi::launch_fused(a, *bufs, q, out, w, true, stream, &wa), "select/attend");

@@ -16,6 +16,9 @@
 //     this step (ordered by (last step, slot id)), as many as there are;
 //     each evicts the slot's previous block from the table and is copied
 //     from the host tier into its slot.
+// slot_order keeps the slots sorted by (last step, slot id): after a step the
+// slots it used (all with the newest step) move to the end, sorted by id, and
+// the others keep their order, so no step sorts more than the slots it used.
 #include "wi_internal.h"
 
 namespace wi {
@@ -23,10 +26,11 @@ namespace {
 
 constexpr int UT = 1024;             // update threads per unit
 constexpr int UW = UT / 64;
-constexpr int MAX_SLOTS = 8192;      // cache slots per unit (LDS sort)
+constexpr int MAX_SLOTS = 8192;      // cache slots per unit (LDS order lists)
 
 __global__ void wb_reset_kernel(int32_t* __restrict__ b2s, int64_t nb, int32_t* __restrict__ s2b,
-                                uint32_t* __restrict__ last, int64_t ns) {
+                                uint32_t* __restrict__ last, int32_t* __restrict__ order,
+                                int64_t ns, int S) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nb;
        i += (int64_t)gridDim.x * blockDim.x)
     b2s[i] = -1;
@@ -34,6 +38,7 @@ __global__ void wb_reset_kernel(int32_t* __restrict__ b2s, int64_t nb, int32_t* 
        i += (int64_t)gridDim.x * blockDim.x) {
     s2b[i] = -1;
     last[i] = 0u;
+    order[i] = (int32_t)(i % S);
   }
 }
 
@@ -65,91 +70,82 @@ __global__ __launch_bounds__(UT) void wb_update_kernel(
     int C, int64_t nblk, int T, int S, const int32_t* __restrict__ size,
     const int32_t* __restrict__ block_off, const uint8_t* __restrict__ zone, uint32_t step,
     int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, uint32_t* __restrict__ last,
-    int32_t* __restrict__ need, int32_t* __restrict__ fill, int32_t* __restrict__ counts,
-    int32_t* __restrict__ stats) {
+    int32_t* __restrict__ order, int32_t* __restrict__ need, int32_t* __restrict__ fill,
+    int32_t* __restrict__ counts, int32_t* __restrict__ stats) {
   const int u = blockIdx.x, tid = threadIdx.x;
   __shared__ int scan_lds[UW];
-  __shared__ uint64_t keys[MAX_SLOTS];
-  __shared__ int s_hit;
+  __shared__ int ord[MAX_SLOTS];   // the slots by (last use, slot id) before this step
+  __shared__ int vic[MAX_SLOTS];   // eviction order of the slots not hit in this step
   const int32_t* sz = size + (int64_t)u * C;
   const int32_t* bo = block_off + (int64_t)u * (C + 1);
   const uint8_t* zn = zone + (int64_t)u * C;
   int32_t* b2su = b2s + (int64_t)u * nblk;
   int32_t* s2bu = s2b + (int64_t)u * S;
   uint32_t* lastu = last + (int64_t)u * S;
+  int32_t* ordu = order + (int64_t)u * S;
   int32_t* needu = need + (int64_t)u * 2 * nblk;  // [needed blocks | misses]
   int32_t* missu = needu + nblk;
   int32_t* fillu = fill + (int64_t)u * 2 * S;
-  if (tid == 0) s_hit = 0;
+  for (int i = tid; i < S; i += UT) ord[i] = ordu[i];
+  // thread t owns the consecutive items [t P, t P + P) of a list of n
+  auto range = [&](int64_t n, int64_t& lo, int64_t& hi) {
+    const int64_t P = (n + UT - 1) / UT;
+    lo = (int64_t)tid * P;
+    hi = lo + P < n ? lo + P : n;
+    if (lo > hi) lo = hi;
+  };
+  int64_t lo, hi;
+  int tot;
 
   // (a) the blocks of the retrieved clusters, ascending
-  int n_need = 0;
-  for (int c0 = 0; c0 < C; c0 += UT) {
-    const int c = c0 + tid;
-    const int nb = (c < C && zn[c] == 1) ? (sz[c] + T - 1) / T : 0;
-    int tot;
-    const int off = wg_scan(nb, scan_lds, &tot);
-    for (int j = 0; j < nb; j++) needu[n_need + off + j] = bo[c] + j;
-    n_need += tot;
+  range(C, lo, hi);
+  int cnt = 0;
+  for (int64_t c = lo; c < hi; c++) cnt += zn[c] == 1 ? (sz[c] + T - 1) / T : 0;
+  int off = wg_scan(cnt, scan_lds, &tot);
+  for (int64_t c = lo; c < hi; c++) {
+    if (zn[c] != 1) continue;
+    const int nb = (sz[c] + T - 1) / T;
+    for (int j = 0; j < nb; j++) needu[off++] = bo[c] + j;
   }
+  const int n_need = tot;
   __syncthreads();
   // (b) hits refresh their slot's step; misses are compacted, ascending
-  int n_miss = 0, hits = 0;
-  for (int i0 = 0; i0 < n_need; i0 += UT) {
-    const int i = i0 + tid;
-    int blk = -1, sl = -1;
-    if (i < n_need) {
-      blk = needu[i];
-      sl = b2su[blk];
-      if (sl >= S) sl = -1;  // (tables written only by this kernel and the reset)
-      if (sl >= 0) {
-        lastu[sl] = step;
-        hits++;
-      }
-    }
-    const int m = (i < n_need && sl < 0) ? 1 : 0;
-    int tot;
-    const int off = wg_scan(m, scan_lds, &tot);
-    if (m) missu[n_miss + off] = blk;
-    n_miss += tot;
-  }
-  atomicAdd(&s_hit, hits);
-  __syncthreads();
-  // (c) eviction order: slots not used in this step by (last step, slot id)
-  int np = 1;
-  while (np < S) np <<= 1;
-  for (int s = tid; s < np; s += UT)
-    keys[s] = (s < S && lastu[s] != step) ? (((uint64_t)lastu[s] << 32) | (uint32_t)s)
-                                          : ~0ull;
-  for (int len = 2; len <= np; len <<= 1) {
-    for (int st = len >> 1; st > 0; st >>= 1) {
-      __syncthreads();
-      for (int i = tid; i < np; i += UT) {
-        const int j = i ^ st;
-        if (j > i) {
-          const bool up = (i & len) == 0;
-          const uint64_t x = keys[i], y = keys[j];
-          if (up ? x > y : x < y) {
-            keys[i] = y;
-            keys[j] = x;
-          }
-        }
-      }
+  range(n_need, lo, hi);
+  int hits = 0;
+  cnt = 0;
+  for (int64_t i = lo; i < hi; i++) {
+    int sl = b2su[needu[i]];
+    if (sl >= S) sl = -1;  // (tables written only by this kernel and the reset)
+    if (sl >= 0) {
+      lastu[sl] = step;
+      hits++;
+    } else {
+      cnt++;
     }
   }
-  __syncthreads();
-  int n_cand = 0;
-  {
-    int c = 0;
-    for (int s = tid; s < S; s += UT) c += keys[s] != ~0ull;
-    int tot;
-    wg_scan(c, scan_lds, &tot);
-    n_cand = tot;
+  off = wg_scan(cnt, scan_lds, &tot);
+  for (int64_t i = lo; i < hi; i++) {
+    const int sl = b2su[needu[i]];
+    if (sl < 0 || sl >= S) missu[off++] = needu[i];
   }
+  const int n_miss = tot;
+  wg_scan(hits, scan_lds, &tot);
+  const int n_hit = tot;
+  __syncthreads();
+  // (c) eviction order: the slots not hit in this step, in (last use, slot
+  // id) order -- the order list with the hit slots taken out
+  range(S, lo, hi);
+  cnt = 0;
+  for (int64_t i = lo; i < hi; i++) cnt += lastu[ord[i]] != step;
+  off = wg_scan(cnt, scan_lds, &tot);
+  for (int64_t i = lo; i < hi; i++)
+    if (lastu[ord[i]] != step) vic[off++] = ord[i];
+  const int n_cand = tot;
+  __syncthreads();
   // (d) admit the misses in order into the eviction order's slots
   const int n_adm = n_miss < n_cand ? n_miss : n_cand;
   for (int i = tid; i < n_adm; i += UT) {
-    const int sl = (int)(uint32_t)(keys[i] & 0xFFFFFFFFull);
+    const int sl = vic[i];
     const int blk = missu[i];
     const int old = s2bu[sl];
     if (old >= 0 && old < nblk) b2su[old] = -1;
@@ -159,13 +155,27 @@ __global__ __launch_bounds__(UT) void wb_update_kernel(
     fillu[2 * i] = blk;
     fillu[2 * i + 1] = sl;
   }
+  __syncthreads();
+  // (e) the new order: the slots not used in this step keep their order,
+  // then the slots used in this step (hits and admissions) by slot id
+  cnt = 0;
+  for (int64_t i = lo; i < hi; i++) cnt += lastu[ord[i]] != step;
+  off = wg_scan(cnt, scan_lds, &tot);
+  for (int64_t i = lo; i < hi; i++)
+    if (lastu[ord[i]] != step) ordu[off++] = ord[i];
+  const int n_keep = tot;
+  cnt = 0;
+  for (int64_t s2 = lo; s2 < hi; s2++) cnt += lastu[s2] == step;
+  off = wg_scan(cnt, scan_lds, &tot);
+  for (int64_t s2 = lo; s2 < hi; s2++)
+    if (lastu[s2] == step) ordu[n_keep + off++] = (int32_t)s2;
   if (tid == 0) {
     counts[u * 4 + 0] = n_need;
-    counts[u * 4 + 1] = s_hit;
+    counts[u * 4 + 1] = n_hit;
     counts[u * 4 + 2] = n_adm;
     counts[u * 4 + 3] = n_miss;
     if (stats) {
-      stats[u * 2 + 0] = s_hit;
+      stats[u * 2 + 0] = n_hit;
       stats[u * 2 + 1] = n_miss;
     }
   }
@@ -204,7 +214,8 @@ int wb_max_slots() { return MAX_SLOTS; }
 
 hipError_t launch_wb_reset(const Geom& g, const WaveBufArgs& wb, hipStream_t s) {
   WI_LAUNCH(K_ZERO, wb_reset_kernel, dim3(256), dim3(256), 0, s, wb.block_slot,
-            (int64_t)g.U * g.cap, wb.slot_block, wb.slot_last, (int64_t)g.U * wb.n_slots);
+            (int64_t)g.U * g.cap, wb.slot_block, wb.slot_last, wb.slot_order,
+            (int64_t)g.U * wb.n_slots, wb.n_slots);
   return hipGetLastError();
 }
 
@@ -214,11 +225,11 @@ hipError_t launch_wb_update(const Geom& g, const WaveBufArgs& wb, const int32_t*
                             hipStream_t s) {
   WI_LAUNCH(K_WB_UPDATE, wb_update_kernel, dim3(g.U), dim3(UT), 0, s, g.C, g.cap, g.T,
             wb.n_slots, cluster_size, block_off, zone, step, wb.block_slot, wb.slot_block,
-            wb.slot_last, need, fill, counts, stats);
+            wb.slot_last, wb.slot_order, need, fill, counts, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int VPB = g.T * D * (g.dtype == WI_BF16 ? 2 : 4) / 16;  // 16-byte pieces per block
-  WI_LAUNCH(K_WB_FILL, wb_fill_kernel, dim3(16, g.U), dim3(256), 0, s,
+  WI_LAUNCH(K_WB_FILL, wb_fill_kernel, dim3(64, g.U), dim3(256), 0, s,
             reinterpret_cast<const uint4*>(wb.host_k), reinterpret_cast<const uint4*>(wb.host_v),
             reinterpret_cast<uint4*>(wb.cache_k), reinterpret_cast<uint4*>(wb.cache_v), fill,
             counts, g.cap, wb.n_slots, VPB);

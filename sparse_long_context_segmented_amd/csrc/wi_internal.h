@@ -238,6 +238,7 @@ struct WaveBufArgs {
   int32_t* block_slot;   // [U][cap]
   int32_t* slot_block;   // [U][n_slots]
   uint32_t* slot_last;   // [U][n_slots]
+  int32_t* slot_order;   // [U][n_slots] slots by (last, slot id)
   void* cache_k;         // [U][n_slots * T][128]
   void* cache_v;
   const void* host_k;    // [U][cap * T][128] in host memory

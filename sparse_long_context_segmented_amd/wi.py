@@ -56,7 +56,8 @@ class IndexBufs(ctypes.Structure):
 class WaveBufferDesc(ctypes.Structure):
     _fields_ = [("n_slots", ctypes.c_int32), ("block_slot", ctypes.c_void_p),
                 ("slot_block", ctypes.c_void_p), ("slot_last", ctypes.c_void_p),
-                ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p)]
+                ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p),
+                ("slot_order", ctypes.c_void_p)]
 
 
 class DecodeDesc(ctypes.Structure):
@@ -389,10 +390,12 @@ class WaveBuffer:
     slot_last: torch.Tensor    # [U, n_slots] int32 (uint32 values)
     cache_k: torch.Tensor      # [U, n_slots * T, 128]
     cache_v: torch.Tensor
+    slot_order: torch.Tensor   # [U, n_slots] int32
 
     def desc(self) -> WaveBufferDesc:
         return WaveBufferDesc(self.n_slots, *[_ptr(t) for t in (
-            self.block_slot, self.slot_block, self.slot_last, self.cache_k, self.cache_v)])
+            self.block_slot, self.slot_block, self.slot_last, self.cache_k, self.cache_v,
+            self.slot_order)])
 
 
 def alloc_wave_buffer(desc: IndexDesc, n_slots: int, device="cuda", stream=None) -> WaveBuffer:
@@ -405,7 +408,8 @@ def alloc_wave_buffer(desc: IndexDesc, n_slots: int, device="cuda", stream=None)
                     torch.empty(U, n_slots, dtype=torch.int32, device=device),
                     torch.empty(U, n_slots, dtype=torch.int32, device=device),
                     torch.empty(U, n_slots * T, 128, dtype=dt, device=device),
-                    torch.empty(U, n_slots * T, 128, dtype=dt, device=device))
+                    torch.empty(U, n_slots * T, 128, dtype=dt, device=device),
+                    torch.empty(U, n_slots, dtype=torch.int32, device=device))
     wd = wb.desc()
     _check(lib().wi_wave_buffer_reset(ctypes.byref(desc), ctypes.byref(wd), _stream(stream)))
     return wb

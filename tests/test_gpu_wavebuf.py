@@ -77,7 +77,10 @@ def _run(w, n_slots_frac, steps, check_every=1, seed_slots=None):
             last = wb.slot_last.cpu().numpy().view(np.uint32)
             ck = wb.cache_k.view(torch.int16).cpu().numpy().reshape(U, n_slots, -1)
             cv = wb.cache_v.view(torch.int16).cpu().numpy().reshape(U, n_slots, -1)
+            order = wb.slot_order.cpu().numpy()
             for u in range(U):
+                assert order[u].tolist() == sorted(range(n_slots),
+                                                   key=lambda s: (sims[u].slot_last[s], s))
                 assert b2s[u].tolist() == sims[u].block_slot, (t, u)
                 assert s2b[u].tolist() == sims[u].slot_block, (t, u)
                 assert last[u].tolist() == sims[u].slot_last, (t, u)
