@@ -229,6 +229,24 @@ wi_status wi_append_token(const wi_index_desc *desc, const wi_index_bufs *bufs,
                           const void *k_new, const void *v_new,
                           hipStream_t stream);
 
+/* Host-only: workspace bytes of wi_append_tokens (2 x U x n_local rows). */
+wi_status wi_append_sizes(const wi_index_desc *desc, size_t *workspace_bytes);
+
+/* n_new tokens per sequence at once -- a prefill chunk, or several decode
+ * steps (framerc blog section 2.1, with section 4.3 problem 3: the index is
+ * built as prefill produces each segment) -- with the same effect as n_new
+ * calls of wi_append_token: with the local window's rows followed by the new
+ * rows, the first n_new become pending rows n_pending .. n_pending + n_new - 1
+ * and the last n_local the new local window.
+ *   k_new, v_new  device [B][H][n_new][128] dtype
+ *   n_new         1 .. seg_len - n_pending (cluster a full segment with
+ *                 wi_extend_index before appending more)
+ *   ws            device workspace of wi_append_sizes bytes
+ * Afterwards the index is described by n_ctx + n_new and n_pending + n_new. */
+wi_status wi_append_tokens(const wi_index_desc *desc, const wi_index_bufs *bufs,
+                           const void *k_new, const void *v_new, int32_t n_new,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Host-only: workspace bytes of wi_extend_index for desc (n_pending =
  * seg_len). */
 wi_status wi_extend_sizes(const wi_index_desc *desc, size_t *workspace_bytes);

@@ -557,6 +557,46 @@ wi_status wi_append_token(const wi_index_desc* desc, const wi_index_bufs* bufs,
   return WI_OK;
 }
 
+wi_status wi_append_sizes(const wi_index_desc* desc, size_t* workspace_bytes) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  if (workspace_bytes)
+    *workspace_bytes = (size_t)align256((int64_t)2 * g.U * g.n_local * wi::D *
+                                        (g.dtype == WI_BF16 ? 2 : 4) + 16);
+  g_err[0] = 0;
+  return WI_OK;
+}
+
+wi_status wi_append_tokens(const wi_index_desc* desc, const wi_index_bufs* bufs,
+                           const void* k_new, const void* v_new, int32_t n_new, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  wi::Geom g;
+  wi_status st = make_geom(desc, &g);
+  if (st != WI_OK) return st;
+  if (n_new < 1 || (int64_t)g.n_pend + n_new > g.seg_len)
+    return fail(WI_E_INVALID, "n_new %d outside [1, seg_len - n_pending = %d]", n_new,
+                g.seg_len - g.n_pend);
+  if (!bufs) return fail(WI_E_INVALID, "bufs is NULL");
+  if (g.n_st > 0) {
+    CHECK_PTR(bufs->steady_k, "bufs->steady_k");
+    CHECK_PTR(bufs->steady_v, "bufs->steady_v");
+  }
+  CHECK_PTR(bufs->pend_k, "bufs->pend_k");
+  CHECK_PTR(bufs->pend_v, "bufs->pend_v");
+  CHECK_PTR(k_new, "k_new");
+  CHECK_PTR(v_new, "v_new");
+  size_t need = 0;
+  st = wi_append_sizes(desc, &need);
+  if (st != WI_OK) return st;
+  if (!ws || ws_bytes < need)
+    return fail(WI_E_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+  if (!aligned16(ws)) return fail(WI_E_INVALID, "ws is not 16-byte aligned");
+  CHECK_HIP(wi::launch_append_many(g, *bufs, k_new, v_new, n_new, ws, stream), "append");
+  g_err[0] = 0;
+  return WI_OK;
+}
+
 wi_status wi_extend_sizes(const wi_index_desc* desc, size_t* workspace_bytes) {
   wi::Geom g, gs;
   wi_status st = make_geom(desc, &g);

@@ -73,6 +73,56 @@ __global__ __launch_bounds__(AT) void append_kernel(uint4* __restrict__ sk, uint
   }
 }
 
+// Many tokens at once (a prefill chunk, or several decode steps): with the
+// local window's rows L[0..n_local) followed by the n_new new rows X, the
+// first n_new rows of (L, X) become pending rows n_pend .. and the last
+// n_local rows of (L, X) the new local window, staged in `stage` first (the
+// window's old rows are still being read).
+__global__ __launch_bounds__(256) void append_many_kernel(
+    const uint4* __restrict__ sk, const uint4* __restrict__ sv, uint4* __restrict__ pk,
+    uint4* __restrict__ pv, const uint4* __restrict__ kn, const uint4* __restrict__ vn,
+    uint4* __restrict__ stk, uint4* __restrict__ stv, int n_sink, int n_local, int n_pend,
+    int seg_len, int n_new, int RV) {
+  const int u = blockIdx.y;
+  const int n_st = n_sink + n_local;
+  const uint4* sku = sk + ((int64_t)u * n_st + n_sink) * RV;  // local rows
+  const uint4* svu = sv + ((int64_t)u * n_st + n_sink) * RV;
+  const uint4* knu = kn + (int64_t)u * n_new * RV;
+  const uint4* vnu = vn + (int64_t)u * n_new * RV;
+  const int64_t total = (int64_t)(n_new + n_local) * RV;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int x = (int)(e / RV), p = (int)(e % RV);  // row x of (L, X)
+    const uint4 k4 = x < n_local ? sku[(int64_t)x * RV + p] : knu[(int64_t)(x - n_local) * RV + p];
+    const uint4 v4 = x < n_local ? svu[(int64_t)x * RV + p] : vnu[(int64_t)(x - n_local) * RV + p];
+    if (x < n_new) {
+      const int64_t d = ((int64_t)u * seg_len + n_pend + x) * RV + p;
+      pk[d] = k4;
+      pv[d] = v4;
+    } else {
+      const int64_t d = ((int64_t)u * n_local + (x - n_new)) * RV + p;
+      stk[d] = k4;
+      stv[d] = v4;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void local_from_stage_kernel(uint4* __restrict__ sk,
+                                                               uint4* __restrict__ sv,
+                                                               const uint4* __restrict__ stk,
+                                                               const uint4* __restrict__ stv,
+                                                               int n_sink, int n_local, int RV) {
+  const int u = blockIdx.y;
+  const int n_st = n_sink + n_local;
+  const int64_t total = (int64_t)n_local * RV;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t d = ((int64_t)u * n_st + n_sink) * RV + e;
+    sk[d] = stk[(int64_t)u * n_local * RV + e];
+    sv[d] = stv[(int64_t)u * n_local * RV + e];
+  }
+}
+
 // A per-unit count: p ? p[u * stride + idx] * mul : c.
 struct Cnt {
   const int32_t* p;
@@ -152,6 +202,30 @@ hipError_t launch_append(const Geom& g, const wi_index_bufs& b, const void* k_ne
             reinterpret_cast<uint4*>(b.pend_k), reinterpret_cast<uint4*>(b.pend_v),
             reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
             g.n_sink, g.n_local, g.n_pend, g.seg_len, RV);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_many(const Geom& g, const wi_index_bufs& b, const void* k_new,
+                              const void* v_new, int n_new, void* stage, hipStream_t s) {
+  const int RV = D * (g.dtype == WI_BF16 ? 2 : 4) / 16;
+  const int64_t total = (int64_t)(n_new + g.n_local) * RV;
+  int gx = (int)((total + 255) / 256);
+  if (gx > 256) gx = 256;
+  const int64_t stage_half = (int64_t)g.U * g.n_local * RV;
+  uint4* stk = reinterpret_cast<uint4*>(stage);
+  uint4* stv = stk + stage_half;
+  WI_LAUNCH(K_APPEND, append_many_kernel, dim3(gx, g.U), dim3(256), 0, s,
+            reinterpret_cast<const uint4*>(b.steady_k), reinterpret_cast<const uint4*>(b.steady_v),
+            reinterpret_cast<uint4*>(b.pend_k), reinterpret_cast<uint4*>(b.pend_v),
+            reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new), stk, stv,
+            g.n_sink, g.n_local, g.n_pend, g.seg_len, n_new, RV);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.n_local == 0) return e;
+  int gl = (int)(((int64_t)g.n_local * RV + 255) / 256);
+  if (gl > 64) gl = 64;
+  WI_LAUNCH(K_APPEND, local_from_stage_kernel, dim3(gl, g.U), dim3(256), 0, s,
+            reinterpret_cast<uint4*>(b.steady_k), reinterpret_cast<uint4*>(b.steady_v), stk, stv,
+            g.n_sink, g.n_local, RV);
   return hipGetLastError();
 }
 

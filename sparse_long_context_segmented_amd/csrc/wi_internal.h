@@ -257,6 +257,9 @@ hipError_t launch_wb_update(const Geom& g, const WaveBufArgs& wb, const int32_t*
                             hipStream_t s);
 hipError_t launch_append(const Geom& g, const wi_index_bufs& b, const void* k_new,
                          const void* v_new, hipStream_t s);
+// n_new tokens at once ([U][n_new][128] rows); stage holds 2 x U x n_local rows.
+hipError_t launch_append_many(const Geom& g, const wi_index_bufs& b, const void* k_new,
+                              const void* v_new, int n_new, void* stage, hipStream_t s);
 // The grown index nw (geometry gn) from the old index o (geometry go) and the
 // new segment sg clustered as a one-segment index (geometry gs).
 hipError_t launch_extend_merge(const Geom& go, const Geom& gn, const Geom& gs,

@@ -22,7 +22,8 @@ WI_POLICY_UNIFORM, WI_POLICY_DENSE_FIRST2, WI_POLICY_BANDED = 0, 1, 2
 STATUS = {0: "WI_OK", 1: "WI_E_INVALID", 2: "WI_E_UNSUPPORTED", 3: "WI_E_WORKSPACE",
           4: "WI_E_HIP"}
 EXPORTS = ("wi_index_sizes", "wi_build_index", "wi_decode_sizes", "wi_decode_attention",
-           "wi_decode_attention_noalloc", "wi_append_token", "wi_extend_sizes",
+           "wi_decode_attention_noalloc", "wi_append_token", "wi_append_sizes",
+           "wi_append_tokens", "wi_extend_sizes",
            "wi_extend_index", "wi_layer_plan", "wi_dense_sizes", "wi_dense_attention",
            "wi_recall_sizes", "wi_recall_at_k", "wi_wave_buffer_reset", "wi_decode_wb_sizes",
            "wi_decode_attention_wb", "wi_status_str", "wi_last_error",
@@ -91,6 +92,10 @@ def lib():
         L.wi_decode_attention_noalloc.restype = ctypes.c_int
         L.wi_append_token.argtypes = [P, P, P, P, P]
         L.wi_append_token.restype = ctypes.c_int
+        L.wi_append_sizes.argtypes = [P, P]
+        L.wi_append_sizes.restype = ctypes.c_int
+        L.wi_append_tokens.argtypes = [P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t, P]
+        L.wi_append_tokens.restype = ctypes.c_int
         L.wi_extend_sizes.argtypes = [P, P]
         L.wi_extend_sizes.restype = ctypes.c_int
         L.wi_extend_index.argtypes = [P, P, P, P, ctypes.c_size_t, P]
@@ -299,6 +304,54 @@ def append_token(index: Index, k_new: torch.Tensor, v_new: torch.Tensor, stream=
     nd.n_ctx += 1
     nd.n_pending += 1
     index.desc = nd
+    return index
+
+
+def append_tokens(index: Index, k_new: torch.Tensor, v_new: torch.Tensor, ws=None,
+                  stream=None) -> Index:
+    """Run wi_append_tokens (k_new, v_new [B, H, n, 128] contiguous, n <=
+    seg_len - n_pending); returns the same buffers under the grown
+    descriptor."""
+    desc = index.desc
+    U = desc.batch * desc.n_kv_heads
+    n = k_new.shape[2]
+    if index.pend_k is None:
+        dt = torch_dtype(desc)
+        index.pend_k = torch.empty(U, desc.seg_len, 128, dtype=dt, device=k_new.device)
+        index.pend_v = torch.empty(U, desc.seg_len, 128, dtype=dt, device=k_new.device)
+    need = ctypes.c_size_t()
+    _check(lib().wi_append_sizes(ctypes.byref(desc), ctypes.byref(need)))
+    if ws is None or ws.numel() < need.value:
+        ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=k_new.device)
+    bufs = index.bufs()
+    _check(lib().wi_append_tokens(ctypes.byref(desc), ctypes.byref(bufs), _ptr(k_new),
+                                  _ptr(v_new), n, _ptr(ws), ws.numel(), _stream(stream)))
+    nd = _copy_desc(desc)
+    nd.n_ctx += n
+    nd.n_pending += n
+    index.desc = nd
+    return index
+
+
+def prefill_chunk(index: Index, k_chunk: torch.Tensor, v_chunk: torch.Tensor,
+                  stream=None) -> Index:
+    """Feed a prefill chunk (k_chunk, v_chunk [B, H, n, 128]) into the index:
+    appended in pieces that end at segment boundaries, each full pending
+    segment clustered (wi_extend_index) as soon as it fills. Returns the
+    (possibly new) index."""
+    n = k_chunk.shape[2]
+    i = 0
+    while i < n:
+        d = index.desc
+        if d.n_pending == d.seg_len:
+            index = extend_index(index, stream=stream)
+            continue
+        m = min(n - i, d.seg_len - d.n_pending)
+        index = append_tokens(index, k_chunk[:, :, i:i + m].contiguous(),
+                              v_chunk[:, :, i:i + m].contiguous(), stream=stream)
+        i += m
+    if index.desc.n_pending == index.desc.seg_len:
+        index = extend_index(index, stream=stream)
     return index
 
 
