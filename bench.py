@@ -49,6 +49,8 @@ def parse():
                     help="bound on the oracle's timed decode loop")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-wb", action="store_true", help="skip the wave-buffer leg")
+    ap.add_argument("--policy", default="uniform", choices=["uniform", "dense-first2", "banded"],
+                    help="per-layer zone policy of a multi-layer model (wi_layer_plan)")
     ap.add_argument("--wg", type=int, default=0,
                     help="fused-kernel workgroups per (sequence, KV head); 0 = automatic")
     ap.add_argument("--profile", action="store_true",
@@ -333,6 +335,12 @@ def model_bench(a, w):
     descs = [wi.make_desc(w.dtype, w.batch, w.n_kv_heads, w.n_ctx, seg_len=w.seg_len,
                           clusters_per_seg=w.clusters_per_seg, n_iters=w.n_iters, layer_id=l)
              for l in range(L)]
+    # the per-layer plan: dense layers keep their raw K/V and build no index
+    pol = {"uniform": wi.WI_POLICY_UNIFORM, "dense-first2": wi.WI_POLICY_DENSE_FIRST2,
+           "banded": wi.WI_POLICY_BANDED}[a.policy]
+    plans = [wi.layer_plan(pol, l, L, w.n_ctx, w.seg_len, w.clusters_per_seg) for l in range(L)]
+    dense = [p[0] == wi.WI_LAYER_DENSE for p in plans]
+    raw = {}
     ns, C, cap, wsb = wi.index_sizes(descs[0])
     ws_build = torch.empty(wsb, dtype=torch.uint8, device=dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -343,6 +351,12 @@ def model_bench(a, w):
         K, V, q = synth.gen_layer_device(w, l, dev)
         torch.cuda.synchronize()
         gen_ms.append((time.perf_counter() - g0) * 1e3)
+        if dense[l]:
+            raw[l] = (K, V)
+            indexes.append(None)
+            qs.append(q)
+            print(f"layer {l}: dense (raw K/V kept)", file=sys.stderr, flush=True)
+            continue
         ix = wi.alloc_index(descs[l], dev)
         if l == L - 1:
             wi.timing_start()
@@ -366,19 +380,29 @@ def model_bench(a, w):
 
     k_r, k_e = w.budgets()
     dd = wi.DecodeDesc(w.n_q_heads, k_r, k_e, 0.0, a.wg)
-    wsd = torch.empty(wi.decode_sizes(descs[0], dd), dtype=torch.uint8, device=dev)
+    dds = [wi.DecodeDesc(w.n_q_heads, p[1], p[2], 0.0, a.wg) for p in plans]
+    ddn = wi.DecodeDesc(w.n_q_heads, 0, 0, 0.0)
+    wsd = torch.empty(max([wi.decode_sizes(descs[0], x) for x, d_ in zip(dds, dense) if not d_]
+                          + [16]), dtype=torch.uint8, device=dev)
+    wsdn = torch.empty(max(wi.dense_sizes(descs[0], ddn), 16), dtype=torch.uint8, device=dev)
     outs = [torch.empty(w.batch, w.n_q_heads, 128, dtype=torch.float32, device=dev)
             for _ in range(L)]
-    nexe = torch.empty(L, U, dtype=torch.int32, device=dev)
+    nexe = torch.zeros(L, U, dtype=torch.int32, device=dev) + 68
     for l in range(L):
-        wi.decode_attention(indexes[l], dd, qs[l], out=outs[l], n_exec=nexe[l], ws=wsd)
+        if dense[l]:
+            wi.dense_attention(descs[l], ddn, *raw[l], qs[l], out=outs[l], ws=wsdn)
+        else:
+            wi.decode_attention(indexes[l], dds[l], qs[l], out=outs[l], n_exec=nexe[l], ws=wsd)
     torch.cuda.synchronize()
     assert all(bool(torch.isfinite(o).all()) for o in outs), "non-finite decode output"
-    retrieved = int((nexe.cpu().numpy() - 68).sum())  # over layers and units
+    retrieved = int((nexe.cpu().numpy() - 68).sum())  # over hybrid layers and units
 
     def step():
         for l in range(L):
-            wi.decode_attention(indexes[l], dd, qs[l], out=outs[l], ws=wsd)
+            if dense[l]:
+                wi.dense_attention(descs[l], ddn, *raw[l], qs[l], out=outs[l], ws=wsdn)
+            else:
+                wi.decode_attention(indexes[l], dds[l], qs[l], out=outs[l], ws=wsd)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -399,14 +423,20 @@ def model_bench(a, w):
 
     G = w.group
     k_e_eff = min(k_e, C - k_r)
-    # algorithmic bytes per launch (one layer), averaged over the layers
+    # algorithmic bytes per launch (one layer), averaged over the hybrid
+    # layers; a dense layer reads every token's K and V
+    Lh = sum(1 for d_ in dense if not d_)
+    ke_l = [min(p[2], C - p[1]) for p, d_ in zip(plans, dense) if not d_]
+    kr_l = [p[1] for p, d_ in zip(plans, dense) if not d_]
     b_score = U * (C * 128 * e + G * 128 * e)
-    b_attend = (U * (k_e_eff * 128 * 4 + (k_r + k_e_eff) * 4 + k_r * 8 + 68 * 128 * e * 2
-                     + G * 128 * 4) + retrieved / L * 128 * e * 2)
-    per_kernel = {"score": b_score, "select_attend": b_attend}
-    dom = max((k for k in avg if per_kernel.get(k, 0) > 0), key=lambda k: avg[k])
+    b_attend = (sum(U * (ke * 128 * 4 + (kr + ke) * 4 + kr * 8 + 68 * 128 * e * 2 + G * 128 * 4)
+                    for kr, ke in zip(kr_l, ke_l)) + retrieved * 128 * e * 2) / max(Lh, 1)
+    b_dense = U * w.n_ctx * 128 * e * 2 + w.batch * w.n_q_heads * 128 * (e + 4)
+    per_kernel = {"score": b_score, "select_attend": b_attend, "dense": b_dense}
+    dom = max((k for k in avg if per_kernel.get(k, 0) > 0), key=lambda k: avg[k] * (
+        (L - Lh) if k == "dense" else Lh))
     achieved = per_kernel[dom] / (avg[dom] * 1e-3) / 1e9
-    step_bytes = L * (b_score + b_attend)
+    step_bytes = Lh * (b_score + b_attend) + (L - Lh) * b_dense
     seg_n = [min(w.seg_len, (w.n_ctx - 68) - s_ * w.seg_len) for s_ in range(ns)]
     flops = sum(2.0 * n * min(w.clusters_per_seg, n) * 128 for n in seg_n) * U
     assign_ms = float(np.mean(bk["assign"]))
@@ -419,7 +449,9 @@ def model_bench(a, w):
         "config": {"workload": w.name, "batch": w.batch, "layers": L, "seq_len": w.n_ctx,
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128,
                    "seg_len": w.seg_len, "clusters_per_seg": w.clusters_per_seg,
-                   "k_retrieve": k_r, "k_estimate": k_e_eff},
+                   "k_retrieve": k_r, "k_estimate": k_e_eff, "policy": a.policy,
+                   "dense_layers": [l for l in range(L) if dense[l]],
+                   "estimate_clusters_per_layer": [p[2] for p in plans]},
         "step_hbm_GBps": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
         "step_bytes": int(step_bytes),
         "resident_GB": round(torch.cuda.memory_allocated(dev) / 1e9, 1),
@@ -430,6 +462,7 @@ def model_bench(a, w):
                      "algorithmic_bytes": {k: int(v) for k, v in per_kernel.items()}},
         "build": {"ms_total": round(float(np.sum(build_ms)), 1),
                   "ms_per_layer": round(float(np.mean(build_ms)), 2),
+                  "layers_built": len(build_ms),
                   "phase_ms_last_layer": {k: round(float(np.sum(v)), 3) for k, v in bk.items()},
                   "assign": {"bound": "mfma",
                              "achieved": round(flops / (assign_ms * 1e-3) / 1e12, 2),
