@@ -75,6 +75,7 @@ constexpr int GRP = 16;            // consecutive cluster ids per ownership grou
 constexpr int EB = 16;             // estimation clusters per wave block
 constexpr int PI_MAX = 32 + EB;    // items per wave block (tokens + clusters)
 constexpr int PART = 2 + D;        // m, l, acc[128]
+constexpr int RM_PLAIN = 0, RM_PEND = 1, RM_CACHED = 2;  // row modes of the fused kernel
 static_assert(NT == 512 && BPT == 4 && KPT % 4 == 0, "thread layout");
 static_assert(CAND_MAX <= 4 * 64 && NW == 8, "four waves rank each pivot's candidates");
 
@@ -221,9 +222,15 @@ struct Lds {
 // Kept a separate instantiation so that the common kernel holds no
 // re-staging loads, after which the compiler would place waits for
 // outstanding loads.
-template <int DT, int GS, bool BIG, bool CACHED>
+// MODE: where the kernel reads rows. RM_PLAIN: steady rows and the HBM block
+// pool only (no pending rows); RM_PEND: also pending rows; RM_CACHED: pending
+// rows, and blocks from the wave buffer's cache slots or the host tier. The
+// plain instantiation keeps the single two-way address select per row.
+template <int DT, int GS, bool BIG, int MODE>
 __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   using L = Lds<GS>;
+  constexpr bool CACHED = MODE == RM_CACHED;
+  constexpr bool PLAIN = MODE == RM_PLAIN;
   constexpr int NTILE = DT == WI_BF16 ? 2 : 1;  // 16-token MFMA tiles per wave block
   constexpr int TB = 16 * NTILE;                // tokens per wave block
   constexpr int PI = TB + EB;                   // items per wave block
@@ -788,9 +795,13 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       for (int j = 0; j < NTILE; j++) {
         if (16 * j < ntw) {
           const int item = t0 + 16 * j + r16;
-          const uint8_t* kp =
-              item < nT ? (item < nS ? xrow(sk8, pk8, rowj[j]) : brow(kb8, ck8, rowj[j], slj[j]))
-                        : dummy;
+          const uint8_t* kp;
+          if constexpr (PLAIN)
+            kp = item < nT ? (item < nS ? sk8 : kb8) + (int64_t)rowj[j] * RB : dummy;
+          else
+            kp = item < nT ? (item < nS ? xrow(sk8, pk8, rowj[j])
+                                        : brow(kb8, ck8, rowj[j], slj[j]))
+                           : dummy;
 #pragma unroll
           for (int s = 0; s < NKL; s++) {
             if constexpr (DT == WI_BF16)
@@ -811,8 +822,12 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
           for (int t = t8; t < t8 + 8; t++) {
             const int row = rdl(rowj[t / 16], t % 16);
             const int sl = CACHED ? rdl(slj[t / 16], t % 16) : -1;
-            const uint8_t* vpt =
-                t < ntw ? (t0 + t < nS ? xrow(sv8, pv8, row) : brow(vb8, cv8, row, sl)) : dummy;
+            const uint8_t* vpt;
+            if constexpr (PLAIN)
+              vpt = t < ntw ? (t0 + t < nS ? sv8 : vb8) + (int64_t)row * RB : dummy;
+            else
+              vpt = t < ntw ? (t0 + t < nS ? xrow(sv8, pv8, row) : brow(vb8, cv8, row, sl))
+                            : dummy;
             if constexpr (DT == WI_BF16)
               vr[t].x = *reinterpret_cast<const uint32_t*>(vpt + 4 * lane);
             else
@@ -1089,22 +1104,28 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   else combine(std::integral_constant<int, MAX_WG>{});
 }
 
-template <int DT, bool BIG, bool CACHED>
+template <int DT, bool BIG, int MODE>
 hipError_t launch_fused_big(const DecodeArgs& da, const FusedArgs& fa, hipStream_t s) {
   dim3 grid(da.W, da.g->U);
   if (da.GS == 4)
-    WI_LAUNCH(K_FUSED, (fused_kernel<DT, 4, BIG, CACHED>), grid, dim3(NT), 0, s, fa);
+    WI_LAUNCH(K_FUSED, (fused_kernel<DT, 4, BIG, MODE>), grid, dim3(NT), 0, s, fa);
   else if (da.GS == 8)
-    WI_LAUNCH(K_FUSED, (fused_kernel<DT, 8, BIG, CACHED>), grid, dim3(NT), 0, s, fa);
+    WI_LAUNCH(K_FUSED, (fused_kernel<DT, 8, BIG, MODE>), grid, dim3(NT), 0, s, fa);
   else
-    WI_LAUNCH(K_FUSED, (fused_kernel<DT, 16, BIG, CACHED>), grid, dim3(NT), 0, s, fa);
+    WI_LAUNCH(K_FUSED, (fused_kernel<DT, 16, BIG, MODE>), grid, dim3(NT), 0, s, fa);
   return hipGetLastError();
 }
 
-template <int DT, bool CACHED>
+template <int DT, int MODE>
 hipError_t launch_fused_dt(const DecodeArgs& da, const FusedArgs& fa, hipStream_t s) {
-  return fa.C > CL ? launch_fused_big<DT, true, CACHED>(da, fa, s)
-                   : launch_fused_big<DT, false, CACHED>(da, fa, s);
+  return fa.C > CL ? launch_fused_big<DT, true, MODE>(da, fa, s)
+                   : launch_fused_big<DT, false, MODE>(da, fa, s);
+}
+
+template <int MODE>
+hipError_t launch_fused_mode(const DecodeArgs& da, const FusedArgs& fa, hipStream_t s) {
+  return da.g->dtype == WI_BF16 ? launch_fused_dt<WI_BF16, MODE>(da, fa, s)
+                                : launch_fused_dt<WI_F32, MODE>(da, fa, s);
 }
 
 }  // namespace
@@ -1155,11 +1176,10 @@ hipError_t launch_fused(const DecodeArgs& da, const wi_index_bufs& bf, const voi
     // the blocks are read from the host tier (device-visible addresses)
     fa.kblk = wb->host_k;
     fa.vblk = wb->host_v;
-    return g.dtype == WI_BF16 ? launch_fused_dt<WI_BF16, true>(da, fa, s)
-                              : launch_fused_dt<WI_F32, true>(da, fa, s);
+    return launch_fused_mode<RM_CACHED>(da, fa, s);
   }
-  return g.dtype == WI_BF16 ? launch_fused_dt<WI_BF16, false>(da, fa, s)
-                            : launch_fused_dt<WI_F32, false>(da, fa, s);
+  return g.n_pend > 0 ? launch_fused_mode<RM_PEND>(da, fa, s)
+                      : launch_fused_mode<RM_PLAIN>(da, fa, s);
 }
 
 }  // namespace wi
