@@ -527,7 +527,8 @@ def wave_buffer_leg(w, desc, ix, dd, qt, q, steps, warmup, fracs=(0.05, 0.10, 0.
         S = max(1, min(8192, int(frac * used)))
         wb = wi.alloc_wave_buffer(desc, S, dev)
         ws = torch.empty(wi.decode_wb_sizes(desc, dd, S), dtype=torch.uint8, device=dev)
-        stats = torch.zeros(warmup + steps, U, 2, dtype=torch.int32, device=dev)
+        # rows padded to an even unit count: each step's [U, 2] slice starts 16-byte aligned
+        stats = torch.zeros(warmup + steps, U + U % 2, 2, dtype=torch.int32, device=dev)
         for i in range(warmup):
             wi.decode_attention_wb(hix, dd, wb, i + 1, qs[i], out=out, stats=stats[i], ws=ws)
         ev0.record(stream)
@@ -535,7 +536,7 @@ def wave_buffer_leg(w, desc, ix, dd, qt, q, steps, warmup, fracs=(0.05, 0.10, 0.
             wi.decode_attention_wb(hix, dd, wb, i + 1, qs[i], out=out, stats=stats[i], ws=ws)
         ev1.record(stream)
         torch.cuda.synchronize()
-        st = stats[warmup:].cpu().numpy().astype(np.int64)
+        st = stats[warmup:, :U].cpu().numpy().astype(np.int64)
         hits, misses = int(st[:, :, 0].sum()), int(st[:, :, 1].sum())
         # kernel durations of the same steps replayed on a second cache (the
         # timing hook's events would perturb the timed loop above)
