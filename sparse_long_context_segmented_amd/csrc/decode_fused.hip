@@ -45,8 +45,12 @@
 //     16 query-head columns (bf16 keys: exact products, fp32 sums);
 //     estimation clusters bring their logits from the score step. Each wave
 //     keeps an online softmax per head (running maximum, denominator in which
-//     an estimation cluster counts n_c times, and two dims per lane of
-//     sum_i p_i v_i over token values and value sums VS_c).
+//     an estimation cluster counts n_c times, and the numerator sum_i p_i v_i
+//     over token values and value sums VS_c). With bf16 values and head
+//     groups of up to 8 the numerator is a second MFMA chain per block: the
+//     weights (split into two bf16 parts) against the tokens' values, each
+//     lane reading 16 contiguous bytes per token, and against the value sums
+//     (each split into two bf16 parts); otherwise two dims per lane on VALU.
 //  4. Merge: the waves' states are combined in a fixed order; the
 //     workgroup's (m, l, acc) per head is published with agent-coherent
 //     stores and one agent-scope release atomic counts arrivals; the last
@@ -231,6 +235,9 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   using L = Lds<GS>;
   constexpr bool CACHED = MODE == RM_CACHED;
   constexpr bool PLAIN = MODE == RM_PLAIN;
+  // token weights-by-values on MFMA (bf16 values, head groups of up to 4;
+  // larger groups keep the VALU path, whose registers then fit)
+  constexpr bool MPV = DT == WI_BF16 && GS <= 8;
   constexpr int NTILE = DT == WI_BF16 ? 2 : 1;  // 16-token MFMA tiles per wave block
   constexpr int TB = 16 * NTILE;                // tokens per wave block
   constexpr int PI = TB + EB;                   // items per wave block
@@ -390,18 +397,27 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   {
     uint4 k4[KPT / 4];
     stage_load(0, k4);
-    // every wave reduces the score workgroups' ranges the same way
+    // every wave reduces the score workgroups' ranges the same way; up to 256
+    // ranges per unit arrive in one round trip
     const float2* mmu = a.mm + (int64_t)u * a.NB;
 #pragma unroll 1
-    for (int j = lane; j < a.NB; j += 64) {
-      const float2 r = mmu[j];
-      lo = fminf(lo, r.x);
-      hi = fmaxf(hi, r.y);
+    for (int j0 = 0; j0 < a.NB; j0 += 256) {
+      float2 r[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int j = j0 + 64 * e + lane;
+        r[e] = j < a.NB ? mmu[j] : make_float2(INFINITY, -INFINITY);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        lo = fminf(lo, r[e].x);
+        hi = fmaxf(hi, r[e].y);
+      }
     }
     lo = -wave_max_u(-lo);
     hi = wave_max_u(hi);
-    inv = hi > lo ? (float)NBINS / (hi - lo) : 0.f;
     __syncthreads();  // histogram cleared
+    inv = hi > lo ? (float)NBINS / (hi - lo) : 0.f;
     stage_store(0, k4, true);
     if constexpr (BIG) {
       // passes 1 .. NP-1: pass p + 1 loads while pass p is counted
@@ -680,9 +696,16 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   // maximum, l_run each lane's share of the running denominator. acc[g][.]
   // holds dims 2 lane, 2 lane + 1 of the running numerator of head g.
   float m_run = -INFINITY, l_run = 0.f;
-  float acc[GS][2];
+  // VALU path: acc[g][.] holds dims 2 lane, 2 lane + 1 of the running
+  // numerator of head g. MFMA path: acct[i] element jj holds
+  // O[head 4 kg + jj][dim 8 r16 + i].
+  float acc[MPV ? 1 : GS][2];
 #pragma unroll
-  for (int g = 0; g < GS; g++) acc[g][0] = acc[g][1] = 0.f;
+  for (int g = 0; g < (MPV ? 1 : GS); g++) acc[g][0] = acc[g][1] = 0.f;
+  f32x4_t acct[MPV ? 8 : 1];
+#pragma unroll
+  for (int i = 0; i < (MPV ? 8 : 1); i++) acct[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bool acc_live = false;  // (wave-uniform) acct holds a weighted item
 
   // own clusters in passes of PASS_CHUNKS(GS) chunks of NT: the item lists of
   // a pass's chunks are gathered (appended) before its items run. The first
@@ -814,9 +837,34 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
           for (int s = 0; s < NKL; s++) ka[j][s] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
-      uint2 vr[TB];  // bf16: .x holds dims 2 lane, 2 lane + 1; fp32: both words
+      // values. bf16: in the B layout of the weights-by-values MFMA -- lane
+      // (r16, kg) reads dims 8 r16 .. 8 r16 + 7 (16 bytes) of its eight
+      // tokens tau(kg, s) = 16 (s / 4) + 4 kg + s % 4, s = 0..7, taking each
+      // token's row from the lane that found it; a token past the block reads
+      // nothing and is zero. fp32: two dims per lane of every token.
+      uint4 vt8[MPV ? 8 : 1];
+      uint2 vr[MPV ? 1 : TB];  // fp32: dims 2 lane, 2 lane + 1
+      if constexpr (MPV) {
 #pragma unroll
-      for (int t8 = 0; t8 < TB; t8 += 8) {
+        for (int s = 0; s < 8; s++) {
+          const int tok = 16 * (s >> 2) + 4 * kg + (s & 3);
+          vt8[s] = make_uint4(0u, 0u, 0u, 0u);
+          if (16 * (s >> 2) < ntw) {
+            const int row = __shfl(rowj[s >> 2], tok & 15, 64);
+            const int sl = CACHED ? __shfl(slj[s >> 2], tok & 15, 64) : -1;
+            if (tok < ntw) {
+              const uint8_t* vpt;
+              if constexpr (PLAIN)
+                vpt = (t0 + tok < nS ? sv8 : vb8) + (int64_t)row * RB;
+              else
+                vpt = t0 + tok < nS ? xrow(sv8, pv8, row) : brow(vb8, cv8, row, sl);
+              vt8[s] = *reinterpret_cast<const uint4*>(vpt + 16 * r16);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int t8 = 0; t8 < (MPV ? 0 : TB); t8 += 8) {
         if (t8 < ntw) {
 #pragma unroll
           for (int t = t8; t < t8 + 8; t++) {
@@ -838,9 +886,26 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
           for (int t = t8; t < t8 + 8; t++) vr[t] = make_uint2(0u, 0u);
         }
       }
-      float2 vs[EB];
+      // estimation value sums. MFMA path: lane (r16, kg) reads dims 8 r16 ..
+      // 8 r16 + 7 (32 bytes) of the value sums of clusters e0 + 4 kg + jj,
+      // jj = 0..3 (the clusters whose logits it holds below); VALU path: two
+      // dims per lane of every cluster of the block.
+      uint4 vse[MPV ? 8 : 1];  // [2 jj + half]
+      float2 vs[MPV ? 1 : EB];
+      if constexpr (MPV) {
 #pragma unroll
-      for (int e4 = 0; e4 < EB; e4 += 4) {
+        for (int jj = 0; jj < 4; jj++) {
+          const int e = 4 * kg + jj;
+          vse[2 * jj] = vse[2 * jj + 1] = make_uint4(0u, 0u, 0u, 0u);
+          if (e < new_) {
+            const uint4* vp = reinterpret_cast<const uint4*>(a.vsum + (uC + Eid[e0 + e]) * D + 8 * r16);
+            vse[2 * jj] = vp[0];
+            vse[2 * jj + 1] = vp[1];
+          }
+        }
+      }
+#pragma unroll
+      for (int e4 = 0; e4 < (MPV ? 0 : EB); e4 += 4) {
         if (e4 < new_) {
 #pragma unroll
           for (int e = e4; e < e4 + 4; e++) {
@@ -912,36 +977,124 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       const float alpha = m_run == -INFINITY ? 0.f : ex<DT>(m_run - mx);
       m_run = mx;
       float ls = 0.f;
+      float pt[NTILE][4];  // token weights, head r16, tokens 16 j + 4 kg + jj
 #pragma unroll
       for (int j = 0; j < NTILE; j++) {
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
           const float p = zt[j][jj] == -INFINITY ? 0.f : ex<DT>(zt[j][jj] - mx);
+          pt[j][jj] = p;
           ls += p;
-          if (r16 < GS) pb[(16 * j + 4 * kg + jj) * GS + r16] = p;
+          if (!MPV && r16 < GS) pb[(16 * j + 4 * kg + jj) * GS + r16] = p;
         }
       }
+      float pe[4];  // estimation weights, head r16, clusters e0 + 4 kg + jj
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         const float p = ze[jj] == -INFINITY ? 0.f : ex<DT>(ze[jj] - mx);
+        pe[jj] = p;
         ls = fmaf(me[jj], p, ls);
-        if (r16 < GS) pb[(TB + 4 * kg + jj) * GS + r16] = p;
+        if (!MPV && r16 < GS) pb[(TB + 4 * kg + jj) * GS + r16] = p;
       }
       l_run = fmaf(l_run, alpha, ls);
 #pragma unroll
-      for (int g = 0; g < GS; g++) {
+      for (int g = 0; g < (MPV ? 0 : GS); g++) {
         const float ag = rdlf(alpha, g);
         acc[g][0] *= ag;
         acc[g][1] *= ag;
       }
+      if constexpr (MPV) {
+        // the accumulator's rows are heads 4 kg + jj
+        if (acc_live && __ballot(r16 < G && alpha != 1.f) != 0) {
+          float ah[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) ah[jj] = __shfl(alpha, 4 * kg + jj, 64);
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) acct[i][jj] *= ah[jj];
+          }
+        }
+      }
       // the weights written above are read back by every lane of the wave
       // (a wave's LDS accesses complete in issue order)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // (e) sum_i p_i v_i over the block's tokens, then its estimation clusters
+      if constexpr (!MPV) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      // (e) sum_i p_i v_i over the block's tokens, then its estimation clusters.
+      // MFMA path: per 16 output dims, O[head][dim] += P[head][k] B[k][dim]
+      // over 32 k-slots, the weights split into two bf16 parts (hi: p
+      // truncated, lo: the exact remainder truncated; together within 2^-14
+      // of p). Lane (r16, kg) holds P[head r16][k] for k-slots 8 kg .. 8 kg + 7
+      // and B[k][8 r16 + i] (dim tile i), and receives O[head 4 kg + jj][8 r16
+      // + i] in element jj of acct[i]. Tokens: slot 8 kg + s is token
+      // tau(kg, s), B = its bf16 values. Estimation clusters: slots 8 kg + 2 jj
+      // and 8 kg + 2 jj + 1 are cluster e0 + 4 kg + jj, B = the two bf16 parts
+      // (truncation, truncated remainder) of its float32 value sum.
+      if constexpr (MPV) {
+        if (new_ > 0) {
+          uint32_t ph[4], pl[4];
 #pragma unroll
-      for (int t = 0; t < TB; t++) {
+          for (int jj = 0; jj < 4; jj++) {
+            const uint32_t h0 = __float_as_uint(pe[jj]) & 0xFFFF0000u;
+            const uint32_t r0 = __float_as_uint(pe[jj] - __uint_as_float(h0)) & 0xFFFF0000u;
+            ph[jj] = (h0 >> 16) | h0;
+            pl[jj] = (r0 >> 16) | r0;
+          }
+          const bf16x8_t a_hi = __builtin_bit_cast(bf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+          const bf16x8_t a_lo = __builtin_bit_cast(bf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            uint32_t bv[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+              const uint4 x = vse[2 * jj + (i >> 2)];
+              const uint32_t vb = (i & 3) == 0 ? x.x : (i & 3) == 1 ? x.y : (i & 3) == 2 ? x.z : x.w;
+              const uint32_t hb = vb & 0xFFFF0000u;
+              const uint32_t rb = __float_as_uint(__uint_as_float(vb) - __uint_as_float(hb));
+              bv[jj] = (hb >> 16) | (rb & 0xFFFF0000u);
+            }
+            const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, make_uint4(bv[0], bv[1], bv[2], bv[3]));
+            acct[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, bb, acct[i], 0, 0, 0);
+            acct[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, bb, acct[i], 0, 0, 0);
+          }
+          acc_live = true;
+        }
+        if (ntw > 0) {
+          uint32_t ph[4], pl[4];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const float p0 = pt[q >> 1][2 * (q & 1)], p1 = pt[q >> 1][2 * (q & 1) + 1];
+            const uint32_t h0 = __float_as_uint(p0) & 0xFFFF0000u;
+            const uint32_t h1 = __float_as_uint(p1) & 0xFFFF0000u;
+            const uint32_t r0 = __float_as_uint(p0 - __uint_as_float(h0));
+            const uint32_t r1 = __float_as_uint(p1 - __uint_as_float(h1));
+            ph[q] = (h0 >> 16) | h1;
+            pl[q] = (r0 >> 16) | (r1 & 0xFFFF0000u);
+          }
+          const bf16x8_t a_hi = __builtin_bit_cast(bf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+          const bf16x8_t a_lo = __builtin_bit_cast(bf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            uint32_t bv[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const uint4 x = vt8[2 * q], y = vt8[2 * q + 1];
+              const uint32_t xd = (i >> 1) == 0 ? x.x : (i >> 1) == 1 ? x.y : (i >> 1) == 2 ? x.z : x.w;
+              const uint32_t yd = (i >> 1) == 0 ? y.x : (i >> 1) == 1 ? y.y : (i >> 1) == 2 ? y.z : y.w;
+              bv[q] = __builtin_amdgcn_perm(yd, xd, (i & 1) ? 0x07060302u : 0x05040100u);
+            }
+            const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, make_uint4(bv[0], bv[1], bv[2], bv[3]));
+            acct[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, bb, acct[i], 0, 0, 0);
+            acct[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, bb, acct[i], 0, 0, 0);
+          }
+          acc_live = true;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < (MPV ? 0 : TB); t++) {
         if (t < ntw) {
           float v0, v1;
           if constexpr (DT == WI_BF16) {
@@ -964,7 +1117,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
         }
       }
 #pragma unroll
-      for (int e = 0; e < EB; e++) {
+      for (int e = 0; e < (MPV ? 0 : EB); e++) {
         if (e < new_) {
           const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(pb + (TB + e) * GS);
 #pragma unroll
@@ -979,9 +1132,11 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
         }
       }
       // the next block rewrites the weights only after these reads
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if constexpr (!MPV) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
     }
   };
   chunk(0);
@@ -998,11 +1153,23 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   l_run += __shfl_xor(l_run, 32, 64);
   __syncthreads();  // the item lists and weights are dead; sacc reuses LDS
   float* sacc = reinterpret_cast<float*>(smem + L::SACC);
+  if constexpr (MPV) {
+    // this wave's rows of sacc from the MFMA layout
 #pragma unroll
-  for (int g = 0; g < GS; g++)
-    if (g < G)
-      *reinterpret_cast<float2*>(sacc + (wv * GS + g) * D + 2 * lane) =
-          make_float2(acc[g][0], acc[g][1]);
+    for (int i = 0; i < 8; i++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int hh = 4 * kg + jj;
+        if (hh < G) sacc[(wv * GS + hh) * D + 8 * r16 + i] = acct[i][jj];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GS; g++)
+      if (g < G)
+        *reinterpret_cast<float2*>(sacc + (wv * GS + g) * D + 2 * lane) =
+            make_float2(acc[g][0], acc[g][1]);
+  }
   if (lane < G) {
     wm[wv][lane] = m_run;
     wl[wv][lane] = l_run;
