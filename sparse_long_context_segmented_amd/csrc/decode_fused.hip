@@ -281,13 +281,32 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     w = blockIdx.x;
     u = blockIdx.y;
   }
-  const int b = u / a.H, h = u % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int C = a.C;
+  const uint32_t* keyg = a.key + (int64_t)u * a.Cp;  // 16-byte aligned rows
+  // The selection's first loads -- the keys of pass 0 and up to 256 of the
+  // score workgroups' ranges -- are issued before the rest of the set-up
+  // arithmetic, which then runs while they are in flight. (Rows are padded
+  // to a multiple of 4 keys: a load at i < n stays in the row.)
+  uint4 k4first[KPT / 4];
+#pragma unroll
+  for (int r = 0; r < KPT / 4; r++) {
+    const int i = 4 * (tid + r * NT);
+    k4first[r] = i < min(CL, C) ? *reinterpret_cast<const uint4*>(keyg + i)
+                                : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const float2* mmu = a.mm + (int64_t)u * a.NB;
+  float2 mmr[4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int j = 64 * e + lane;
+    mmr[e] = j < a.NB ? mmu[j] : make_float2(INFINITY, -INFINITY);
+  }
+  const int b = u / a.H, h = u % a.H;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int C = a.C, G = a.G, W = a.W;
+  const int G = a.G, W = a.W;
   const int K_r = a.K_r, K_e = a.K_e;
   const int NP = BIG ? (C + CL - 1) / CL : 1;  // LDS passes over the keys
-  const uint32_t* keyg = a.key + (int64_t)u * a.Cp;  // 16-byte aligned rows
   const int64_t uC = (int64_t)u * C;
   const int n_x = a.n_st + a.n_pend;  // steady rows, then pending rows
   const int s_lo = (int)((int64_t)n_x * w / W), s_hi = (int)((int64_t)n_x * (w + 1) / W);
@@ -299,15 +318,16 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
 
   // ---- prologue: query rows to LDS; the first chunk's own-cluster data into
   // registers. All of these loads are issued before the selection starts. ----
+  // (the query piece of this thread, GS rows of QB bytes in 16-byte pieces,
+  // at most one per thread, goes to LDS once the histogram is built, so that
+  // no wait for it precedes the selection's loads)
+  constexpr int QB = D * (DT == WI_BF16 ? 2 : 4);  // bytes per query row
+  static_assert(GS * QB / 16 <= NT, "one query piece per thread");
+  uint4 qpiece = make_uint4(0u, 0u, 0u, 0u);
   {
-    constexpr int QB = D * (DT == WI_BF16 ? 2 : 4);  // bytes per query row
     const uint8_t* qg = reinterpret_cast<const uint8_t*>(a.q) +
                         ((int64_t)b * a.Hq + (int64_t)h * G) * QB;
-    for (int i = tid; i < GS * QB / 16; i += NT) {
-      const int row = i / (QB / 16);
-      const uint4 v = row < G ? reinterpret_cast<const uint4*>(qg)[i] : make_uint4(0u, 0u, 0u, 0u);
-      reinterpret_cast<uint4*>(qs)[i] = v;
-    }
+    if (tid < GS * QB / 16 && tid / (QB / 16) < G) qpiece = reinterpret_cast<const uint4*>(qg)[tid];
   }
   int sz0, blk0;
   f32x4_t sl0[GS / 4];
@@ -337,20 +357,19 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int r = 0; r < KPT / 4; r++) {
       const int i = 4 * (tid + r * NT);
-      if (i < n) {
-        *reinterpret_cast<uint4*>(keys + i) = k4[r];
-        if (count) {
-          const uint32_t kk[4] = {k4[r].x, k4[r].y, k4[r].z, k4[r].w};
-          int bn[4];
+      if (i < n) *reinterpret_cast<uint4*>(keys + i) = k4[r];
+      if (count) {
+        const uint32_t kk[4] = {k4[r].x, k4[r].y, k4[r].z, k4[r].w};
+        int bn[4];
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            bn[e] = bin_of(kk[e], lo, inv);
-            if (i + e < n) atomicAdd(&hist[bn[e]], 1);
-          }
-          // (pass 0's bins are kept for the candidate scan of a one-pass unit)
-          *reinterpret_cast<uint2*>(kbin + i) =
-              make_uint2((uint32_t)bn[0] | ((uint32_t)bn[1] << 16), (uint32_t)bn[2] | ((uint32_t)bn[3] << 16));
+        for (int e = 0; e < 4; e++) {
+          bn[e] = i + e < n ? bin_of(kk[e], lo, inv) : 0xFFFF;  // (no bin: never a pivot's)
+          if (i + e < n) atomicAdd(&hist[bn[e]], 1);
         }
+        // (pass 0's bins are kept for the candidate scan of a one-pass unit;
+        // every slot of the CL-entry array is written)
+        *reinterpret_cast<uint2*>(kbin + i) =
+            make_uint2((uint32_t)bn[0] | ((uint32_t)bn[1] << 16), (uint32_t)bn[2] | ((uint32_t)bn[3] << 16));
       }
     }
   };
@@ -396,12 +415,16 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   }
   {
     uint4 k4[KPT / 4];
-    stage_load(0, k4);
-    // every wave reduces the score workgroups' ranges the same way; up to 256
-    // ranges per unit arrive in one round trip
-    const float2* mmu = a.mm + (int64_t)u * a.NB;
+#pragma unroll
+    for (int r = 0; r < KPT / 4; r++) k4[r] = k4first[r];
+    // every wave reduces the score workgroups' ranges the same way
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      lo = fminf(lo, mmr[e].x);
+      hi = fmaxf(hi, mmr[e].y);
+    }
 #pragma unroll 1
-    for (int j0 = 0; j0 < a.NB; j0 += 256) {
+    for (int j0 = 256; j0 < a.NB; j0 += 256) {
       float2 r[4];
 #pragma unroll
       for (int e = 0; e < 4; e++) {
@@ -432,6 +455,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       }
     }
   }
+  if (tid < GS * QB / 16) reinterpret_cast<uint4*>(qs)[tid] = qpiece;
   __syncthreads();
 
   // ---- 1c. pivot bins: thread t owns bins NBINS-1-4t down to NBINS-4-4t ----
@@ -544,44 +568,77 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   }
 
   // ---- 1d. keys of the pivot bins -------------------------------------------
-  // pass p's keys: from LDS (one pass) or from registers k4r (C > CL)
+  // pass p's keys: from LDS (one pass) or from registers k4r (C > CL). A
+  // thread's bins are read (or computed) first; each wave then takes the
+  // slots of its hits with one LDS atomic per target and writes them.
   auto cand_scan = [&](int p, const uint4* k4r) {
     const int n = min(CL, C - p * CL);
+    int bns[KPT];
 #pragma unroll
     for (int r = 0; r < KPT / 4; r++) {
       const int i = 4 * (tid + r * NT);
-      if (i >= n) continue;
-      int bns[4];
       if (k4r) {
         const uint32_t kr[4] = {k4r[r].x, k4r[r].y, k4r[r].z, k4r[r].w};
 #pragma unroll
-        for (int e = 0; e < 4; e++) bns[e] = bin_of(kr[e], lo, inv);
+        for (int e = 0; e < 4; e++) bns[4 * r + e] = i + e < n ? bin_of(kr[e], lo, inv) : -2;
       } else {
+        // (keys past the unit carry the no-bin mark)
         const uint2 bb = *reinterpret_cast<const uint2*>(kbin + i);
-        bns[0] = bb.x & 0xFFFF;
-        bns[1] = bb.x >> 16;
-        bns[2] = bb.y & 0xFFFF;
-        bns[3] = bb.y >> 16;
+        bns[4 * r] = (int)(bb.x & 0xFFFF);
+        bns[4 * r + 1] = (int)(bb.x >> 16);
+        bns[4 * r + 2] = (int)(bb.y & 0xFFFF);
+        bns[4 * r + 3] = (int)(bb.y >> 16);
       }
-      const bool any = (bns[0] == b1) | (bns[1] == b1) | (bns[2] == b1) | (bns[3] == b1) |
-                       (bns[0] == b2) | (bns[1] == b2) | (bns[2] == b2) | (bns[3] == b2);
-      if (!any) continue;
-      const uint4 k4 = k4r ? k4r[r] : *reinterpret_cast<const uint4*>(keys + i);
-      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+    }
+    // hit masks in vector registers (bit k: key k of this thread)
+    uint32_t m0 = 0u, m1 = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        if (i + e < n) {
+    for (int k = 0; k < KPT; k++) {
+      m0 |= (bns[k] == b1 ? 1u : 0u) << k;
+      m1 |= (bns[k] == b2 ? 1u : 0u) << k;
+    }
+    const int c0 = __popc(m0), c1 = __popc(m1);
+    const int i0 = wave_incl_scan(c0), i1 = wave_incl_scan(c1);
+    const int t0 = rdl(i0, 63), t1 = rdl(i1, 63);
+    if (t0 + t1 == 0) return;  // (wave-uniform)
+    int base0 = 0, base1 = 0;
+    if (lane == 0) {
+      if (t0) base0 = atomicAdd(&ncand[0], t0);
+      if (t1) base1 = atomicAdd(&ncand[1], t1);
+    }
+    int s0 = rdl(base0, 0) + i0 - c0, s1 = rdl(base1, 0) + i1 - c1;
+    // this thread's hits, in key order (a later pass's keys are picked out of
+    // the registers, so that no load is waited for here)
+    uint32_t mm = m0 | m1;
+    while (mm) {
+      const int k = __builtin_ctz(mm);
+      mm &= mm - 1u;
+      const int idx = 4 * (tid + (k >> 2) * NT) + (k & 3);
+      uint32_t kk;
+      if (k4r) {
+        kk = 0u;
 #pragma unroll
-          for (int t = 0; t < 2; t++) {
-            if (bns[e] == (t == 0 ? b1 : b2)) {
-              const int s = atomicAdd(&ncand[t], 1);
-              if (s < CAND_MAX) {
-                candk[t * CAND_MAX + s] = kk[e];
-                candi[t * CAND_MAX + s] = p * CL + i + e;
-              }
-            }
-          }
+        for (int j = 0; j < KPT; j++) {
+          const uint4 q4 = k4r[j >> 2];
+          const uint32_t x = (j & 3) == 0 ? q4.x : (j & 3) == 1 ? q4.y : (j & 3) == 2 ? q4.z : q4.w;
+          kk = k == j ? x : kk;
         }
+      } else {
+        kk = keys[idx];
+      }
+      if ((m0 >> k) & 1u) {
+        if (s0 < CAND_MAX) {
+          candk[s0] = kk;
+          candi[s0] = p * CL + idx;
+        }
+        s0++;
+      }
+      if ((m1 >> k) & 1u) {
+        if (s1 < CAND_MAX) {
+          candk[CAND_MAX + s1] = kk;
+          candi[CAND_MAX + s1] = p * CL + idx;
+        }
+        s1++;
       }
     }
   };
