@@ -180,9 +180,11 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 // Monotone in the key (ties share a bin); NaN values land in bin 0.
-__device__ __forceinline__ int bin_of(uint32_t k, float lo, float inv) {
-  const float x = (key_value(k) - lo) * inv;
-  return x >= 1.f ? (int)fminf(x, (float)(NBINS - 1)) : 0;
+// off = -lo * inv. fma is monotone in the value for inv >= 0, so equal keys
+// share a bin and bins follow key order; the median clamps to [0, NBINS - 1]
+// (a NaN value lands in bin 0).
+__device__ __forceinline__ int bin_of(uint32_t k, float off, float inv) {
+  return (int)__builtin_amdgcn_fmed3f(fmaf(key_value(k), inv, off), 0.f, (float)(NBINS - 1));
 }
 __device__ __forceinline__ uint64_t comp_of(uint32_t k, int id) {
   return ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
@@ -203,8 +205,8 @@ constexpr int PASS_CHUNKS(int GS) { return GS <= 4 ? 4 : (GS <= 8 ? 2 : 1); }
 template <int GS>
 struct Lds {
   static constexpr int KEYS = 0;                              // uint32[CL]
-  static constexpr int HIST = KEYS + CL * 4;                  // int[NBINS]
-  static constexpr int CANDK = HIST + NBINS * 4;              // uint32[2][CAND_MAX]
+  static constexpr int HIST = KEYS + CL * 4;                  // int[NBINS + 1] (+ spare slot)
+  static constexpr int CANDK = HIST + (NBINS + 4) * 4;        // uint32[2][CAND_MAX]
   static constexpr int CANDI = CANDK + 2 * CAND_MAX * 4;      // int[2][CAND_MAX]
   static constexpr int BINS = CANDI + 2 * CAND_MAX * 4;       // uint16[CL] histogram bin per key
   static constexpr int LN = NT * PASS_CHUNKS(GS);             // list capacity
@@ -275,8 +277,9 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   if ((gridDim.y & 7) == 0) {
     const int L = (int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x;
     const int slot = L >> 3;
-    u = (slot / (int)gridDim.x) * 8 + (L & 7);
-    w = slot % (int)gridDim.x;
+    const int q = slot / (int)gridDim.x;
+    u = q * 8 + (L & 7);
+    w = slot - q * (int)gridDim.x;
   } else {
     w = blockIdx.x;
     u = blockIdx.y;
@@ -302,14 +305,16 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     const int j = 64 * e + lane;
     mmr[e] = j < a.NB ? mmu[j] : make_float2(INFINITY, -INFINITY);
   }
-  const int b = u / a.H, h = u % a.H;
+  const int b = u / a.H, h = u - b * a.H;
   const int r16 = lane & 15, kg = lane >> 4;
   const int G = a.G, W = a.W;
   const int K_r = a.K_r, K_e = a.K_e;
   const int NP = BIG ? (C + CL - 1) / CL : 1;  // LDS passes over the keys
   const int64_t uC = (int64_t)u * C;
   const int n_x = a.n_st + a.n_pend;  // steady rows, then pending rows
-  const int s_lo = (int)((int64_t)n_x * w / W), s_hi = (int)((int64_t)n_x * (w + 1) / W);
+  // (32-bit products whenever they fit: a 64-bit division is ~150 instructions)
+  const int s_lo = n_x < (1 << 24) ? n_x * w / W : (int)((int64_t)n_x * w / W);
+  const int s_hi = n_x < (1 << 24) ? n_x * (w + 1) / W : (int)((int64_t)n_x * (w + 1) / W);
   // own groups w, w + W, ... of the ng groups; own index k -> cluster id
   const int ng = (C + GRP - 1) / GRP;
   const int n_own = ng > w ? ((ng - 1 - w) / W + 1) * GRP : 0;
@@ -351,20 +356,24 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       k4[r] = i < n ? *reinterpret_cast<const uint4*>(keyg + c0 + i) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  float lo = INFINITY, hi = -INFINITY, inv = 0.f;
+  float lo = INFINITY, hi = -INFINITY, inv = 0.f, off = 0.f;
   auto stage_store = [&](int p, const uint4* k4, bool count) {
     const int n = min(CL, C - p * CL);
 #pragma unroll
     for (int r = 0; r < KPT / 4; r++) {
       const int i = 4 * (tid + r * NT);
-      if (i < n) *reinterpret_cast<uint4*>(keys + i) = k4[r];
+      *reinterpret_cast<uint4*>(keys + i) = k4[r];  // (i < CL: slots past the unit unused)
       if (count) {
         const uint32_t kk[4] = {k4[r].x, k4[r].y, k4[r].z, k4[r].w};
         int bn[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          bn[e] = i + e < n ? bin_of(kk[e], lo, inv) : 0xFFFF;  // (no bin: never a pivot's)
-          if (i + e < n) atomicAdd(&hist[bn[e]], 1);
+          // keys past the unit count in the spare slot hist[NBINS] and carry
+          // the no-bin mark (never a pivot's)
+          const bool ok = i + e < n;
+          const int bb = bin_of(kk[e], off, inv);
+          bn[e] = ok ? bb : 0xFFFF;
+          atomicAdd(&hist[ok ? bb : NBINS], 1);
         }
         // (pass 0's bins are kept for the candidate scan of a one-pass unit;
         // every slot of the CL-entry array is written)
@@ -391,8 +400,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       const int i = 4 * (tid + r * NT);
       const uint32_t kk[4] = {k4[r].x, k4[r].y, k4[r].z, k4[r].w};
 #pragma unroll
-      for (int e = 0; e < 4; e++)
-        if (i + e < n) atomicAdd(&hist[bin_of(kk[e], lo, inv)], 1);
+      for (int e = 0; e < 4; e++) atomicAdd(&hist[i + e < n ? bin_of(kk[e], off, inv) : NBINS], 1);
     }
   };
   // re-stage pass p for a later scan (C > CL only); leaves keys ready in LDS
@@ -441,6 +449,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     hi = wave_max_u(hi);
     __syncthreads();  // histogram cleared
     inv = hi > lo ? (float)NBINS / (hi - lo) : 0.f;
+    off = -lo * inv;
     stage_store(0, k4, true);
     if constexpr (BIG) {
       // passes 1 .. NP-1: pass p + 1 loads while pass p is counted
@@ -533,7 +542,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   {
     const int id0 = own_id(tid);
     const bool ok = tid < n_own && id0 < C && sz0 > 0;
-    const int bn = ok ? bin_of(NP == 1 ? keys[id0] : keyg[id0], lo, inv) : -1;
+    const int bn = ok ? bin_of(NP == 1 ? keys[id0] : keyg[id0], off, inv) : -1;
     const bool maybeS = ok && (M1 >= C || (need1 && bn >= b2));
     const bool maybeR = ok && (M0 >= C || (need0 && bn >= b1));
     const bool surelyR = ok && (M0 >= C || (need0 && bn > b1));
@@ -580,7 +589,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       if (k4r) {
         const uint32_t kr[4] = {k4r[r].x, k4r[r].y, k4r[r].z, k4r[r].w};
 #pragma unroll
-        for (int e = 0; e < 4; e++) bns[4 * r + e] = i + e < n ? bin_of(kr[e], lo, inv) : -2;
+        for (int e = 0; e < 4; e++) bns[4 * r + e] = i + e < n ? bin_of(kr[e], off, inv) : -2;
       } else {
         // (keys past the unit carry the no-bin mark)
         const uint2 bb = *reinterpret_cast<const uint2*>(kbin + i);
@@ -711,7 +720,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
 #pragma unroll 1
           for (int i = tid; i < n; i += NT) {
             const uint32_t kk = keys[i];
-            if (bin_of(kk, lo, inv) == bs) {
+            if (bin_of(kk, off, inv) == bs) {
               const uint64_t comp = comp_of(kk, p * CL + i);
               if (d == 0 || (comp >> (shift + 8)) == (pref >> (shift + 8)))
                 atomicAdd(&rdx[(comp >> shift) & 255], 1);
