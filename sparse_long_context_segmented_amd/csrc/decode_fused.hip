@@ -205,8 +205,8 @@ constexpr int PASS_CHUNKS(int GS) { return GS <= 4 ? 4 : (GS <= 8 ? 2 : 1); }
 template <int GS>
 struct Lds {
   static constexpr int KEYS = 0;                              // uint32[CL]
-  static constexpr int HIST = KEYS + CL * 4;                  // int[NBINS + 1] (+ spare slot)
-  static constexpr int CANDK = HIST + (NBINS + 4) * 4;        // uint32[2][CAND_MAX]
+  static constexpr int HIST = KEYS + CL * 4;                  // int[NBINS + 64] (+ spare slots)
+  static constexpr int CANDK = HIST + (NBINS + 64) * 4;       // uint32[2][CAND_MAX]
   static constexpr int CANDI = CANDK + 2 * CAND_MAX * 4;      // int[2][CAND_MAX]
   static constexpr int BINS = CANDI + 2 * CAND_MAX * 4;       // uint16[CL] histogram bin per key
   static constexpr int LN = NT * PASS_CHUNKS(GS);             // list capacity
@@ -368,12 +368,13 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
         int bn[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          // keys past the unit count in the spare slot hist[NBINS] and carry
+          // keys past the unit count in the lane's spare slot hist[NBINS +
+          // lane] (one per lane: no two lanes of an atomic share it) and carry
           // the no-bin mark (never a pivot's)
           const bool ok = i + e < n;
           const int bb = bin_of(kk[e], off, inv);
           bn[e] = ok ? bb : 0xFFFF;
-          atomicAdd(&hist[ok ? bb : NBINS], 1);
+          atomicAdd(&hist[ok ? bb : NBINS + lane], 1);
         }
         // (pass 0's bins are kept for the candidate scan of a one-pass unit;
         // every slot of the CL-entry array is written)
@@ -400,7 +401,8 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       const int i = 4 * (tid + r * NT);
       const uint32_t kk[4] = {k4[r].x, k4[r].y, k4[r].z, k4[r].w};
 #pragma unroll
-      for (int e = 0; e < 4; e++) atomicAdd(&hist[i + e < n ? bin_of(kk[e], off, inv) : NBINS], 1);
+      for (int e = 0; e < 4; e++)
+        atomicAdd(&hist[i + e < n ? bin_of(kk[e], off, inv) : NBINS + lane], 1);
     }
   };
   // re-stage pass p for a later scan (C > CL only); leaves keys ready in LDS
