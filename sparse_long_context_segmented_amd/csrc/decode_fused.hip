@@ -828,10 +828,18 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
         const int idc = k < n_own && id < C ? id : 0;
         const int n = a.size[uC + idc];
         const int blk = a.block_off[(int64_t)u * (C + 1) + idc];
+        // estimation logits only for estimation clusters when the key is on
+        // chip (one key pass); with several passes the key would cost one
+        // more round trip, so every own cluster's logits are read
+        bool wantS = true;
+        if constexpr (!BIG) {
+          const uint64_t comp = comp_of(keys[idc], id);
+          wantS = !noneS && comp >= cS && (noneR || comp < cR);
+        }
         f32x4_t sl[GS / 4];
         const f32x4_t* sp = reinterpret_cast<const f32x4_t*>(a.S + (uC + idc) * GS);
 #pragma unroll
-        for (int g4 = 0; g4 < GS / 4; g4++) sl[g4] = sp[g4];
+        for (int g4 = 0; g4 < GS / 4; g4++) sl[g4] = wantS ? sp[g4] : f32x4_t{0.f, 0.f, 0.f, 0.f};
         setup(ch, n, blk, sl);
       }
     }
