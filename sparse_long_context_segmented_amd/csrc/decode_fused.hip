@@ -206,9 +206,8 @@ template <int GS>
 struct Lds {
   static constexpr int KEYS = 0;                              // uint32[CL]
   static constexpr int HIST = KEYS + CL * 4;                  // int[NBINS + 64] (+ spare slots)
-  static constexpr int CANDK = HIST + (NBINS + 64) * 4;       // uint32[2][CAND_MAX]
-  static constexpr int CANDI = CANDK + 2 * CAND_MAX * 4;      // int[2][CAND_MAX]
-  static constexpr int BINS = CANDI + 2 * CAND_MAX * 4;       // uint16[CL] histogram bin per key
+  static constexpr int CAND = HIST + (NBINS + 64) * 4;        // uint64[2][CAND_MAX] comps
+  static constexpr int BINS = CAND + 2 * CAND_MAX * 8;        // uint16[CL] histogram bin per key
   static constexpr int LN = NT * PASS_CHUNKS(GS);             // list capacity
   static constexpr int RTOK = BINS + CL * 2;                  // int[LN + 4]
   static constexpr int RBLK = RTOK + (LN + 4) * 4;            // int[LN]
@@ -221,7 +220,7 @@ struct Lds {
   static constexpr int SACC = 0;                              // float[NW][GS][D]
   static constexpr int END_MERGE = SACC + NW * GS * D * 4;
   static constexpr int BYTES = END > END_MERGE ? END : END_MERGE;
-  static_assert(RTOK % 16 == 0 && PBUF % 16 == 0 && QS % 16 == 0, "align");
+  static_assert(CAND % 16 == 0 && RTOK % 16 == 0 && PBUF % 16 == 0 && QS % 16 == 0, "align");
 };
 
 // BIG: more than CL clusters per unit (keys staged in several LDS passes).
@@ -248,8 +247,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   __shared__ __align__(16) uint8_t smem[L::BYTES];
   uint32_t* keys = reinterpret_cast<uint32_t*>(smem + L::KEYS);
   int* hist = reinterpret_cast<int*>(smem + L::HIST);
-  uint32_t* candk = reinterpret_cast<uint32_t*>(smem + L::CANDK);
-  int* candi = reinterpret_cast<int*>(smem + L::CANDI);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem + L::CAND);  // pivot-bin comps
   uint16_t* kbin = reinterpret_cast<uint16_t*>(smem + L::BINS);
   int* Rtok = reinterpret_cast<int*>(smem + L::RTOK);
   int* Rblk = reinterpret_cast<int*>(smem + L::RBLK);
@@ -417,12 +415,10 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   // ---- 1a.-1b. key range (from the score step) and histogram -----------------
   for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
   if (tid < 2) ncand[tid] = 0;
-  // candidate lists start as entries that never rank above a candidate (key
-  // 0, id INT_MAX), so the ranking can read them four at a time past nc
-  for (int i = tid; i < 2 * CAND_MAX; i += NT) {
-    candk[i] = 0u;
-    candi[i] = INT_MAX;
-  }
+  // candidate lists start as comps 0, below every candidate's (whose low word
+  // 2^32 - 1 - id is positive), so the ranking can read them four at a time
+  // past nc
+  for (int i = tid; i < 2 * CAND_MAX; i += NT) cand[i] = 0ull;
   {
     uint4 k4[KPT / 4];
 #pragma unroll
@@ -639,15 +635,13 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       }
       if ((m0 >> k) & 1u) {
         if (s0 < CAND_MAX) {
-          candk[s0] = kk;
-          candi[s0] = p * CL + idx;
+          cand[s0] = comp_of(kk, p * CL + idx);
         }
         s0++;
       }
       if ((m1 >> k) & 1u) {
         if (s1 < CAND_MAX) {
-          candk[CAND_MAX + s1] = kk;
-          candi[CAND_MAX + s1] = p * CL + idx;
+          cand[CAND_MAX + s1] = comp_of(kk, p * CL + idx);
         }
         s1++;
       }
@@ -671,9 +665,10 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // ---- 1e. pivots: waves 4t .. 4t + 3 rank the keys of target t's bin, one
+  // ---- 1e. pivots: waves 4t .. 4t + 3 rank the comps of target t's bin, one
   // candidate per lane (candidate 64 (wv % 4) + lane), comparing against
-  // four candidates per pair of LDS broadcast reads --------------------------
+  // four candidates per pair of LDS broadcast reads, one 64-bit compare each
+  // (rank = number of larger comps; distinct ids make comps distinct) -------
   const int nc0 = ncand[0], nc1 = ncand[1];
   {
     const int t = wv >> 2, qw = wv & 3;
@@ -681,23 +676,19 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     const int nc = t == 0 ? nc0 : nc1;
     if (need && nc <= CAND_MAX && 64 * qw < nc) {
       const int i = 64 * qw + lane;
-      const uint32_t kk = i < nc ? candk[t * CAND_MAX + i] : 0u;
-      const int id = i < nc ? candi[t * CAND_MAX + i] : INT_MAX;
+      const uint64_t mine = i < nc ? cand[t * CAND_MAX + i] : 0ull;
       int rank = 0;
-      const uint4* ck = reinterpret_cast<const uint4*>(candk + t * CAND_MAX);
-      const int4* ci = reinterpret_cast<const int4*>(candi + t * CAND_MAX);
+      const uint64_t* ct = cand + t * CAND_MAX;
 #pragma unroll 4
       for (int j4 = 0; j4 < (nc + 3) / 4; j4++) {
-        const uint4 k4 = ck[j4];
-        const int4 i4 = ci[j4];
-        rank += (k4.x > kk) || (k4.x == kk && i4.x < id);
-        rank += (k4.y > kk) || (k4.y == kk && i4.y < id);
-        rank += (k4.z > kk) || (k4.z == kk && i4.z < id);
-        rank += (k4.w > kk) || (k4.w == kk && i4.w < id);
+        // (entries past nc are zero and never larger)
+        const ulonglong2 c01 = reinterpret_cast<const ulonglong2*>(ct)[2 * j4];
+        const ulonglong2 c23 = reinterpret_cast<const ulonglong2*>(ct)[2 * j4 + 1];
+        rank += (c01.x > mine) + (c01.y > mine) + (c23.x > mine) + (c23.y > mine);
       }
       if (i < nc && rank == bneed[t] - 1) {
-        pk[t] = kk;
-        pi[t] = id;
+        pk[t] = (uint32_t)(mine >> 32);
+        pi[t] = (int)(0xFFFFFFFFu - (uint32_t)mine);
       }
     }
   }
