@@ -790,23 +790,25 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       const bool inE = inS && !inR;
       if (a.zone && ok) a.zone[uC + id] = inR ? 1 : (inE ? 2 : 0);
       const bool rT = inR && n > 0, eT = inE && n > 0;  // zones with members
-      const int v3[3] = {(int)rT, rT ? n : 0, (int)eT};
-      int off3[3], tot3[3];
-      block_scan<3>(v3, off3, tot3, scan_lds);
+      // (the two flags share one scanned int: at most NT of each per chunk)
+      const int v2[2] = {(int)rT | ((int)eT << 16), rT ? n : 0};
+      int off2[2], tot2[2];
+      block_scan<2>(v2, off2, tot2, scan_lds);
+      const int oR = off2[0] & 0xFFFF, oE = off2[0] >> 16;
       if (rT) {
-        Rtok[nR + off3[0]] = nRtok + off3[1];
-        Rblk[nR + off3[0]] = blk;
+        Rtok[nR + oR] = nRtok + off2[1];
+        Rblk[nR + oR] = blk;
       }
       if (eT) {
-        Eid[nE + off3[2]] = id;
-        Esz[nE + off3[2]] = (float)n;
-        float* el = Elog + (nE + off3[2]) * GS;
+        Eid[nE + oE] = id;
+        Esz[nE + oE] = (float)n;
+        float* el = Elog + (nE + oE) * GS;
 #pragma unroll
         for (int g4 = 0; g4 < GS / 4; g4++) *reinterpret_cast<f32x4_t*>(el + 4 * g4) = sl[g4];
       }
-      nR += tot3[0];
-      nRtok += tot3[1];
-      nE += tot3[2];
+      nR += tot2[0] & 0xFFFF;
+      nRtok += tot2[1];
+      nE += tot2[0] >> 16;
     };
     const int c1 = min(c0 + PC, n_chunks);
 #pragma unroll 1
@@ -852,19 +854,27 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
       const int ntw = max(0, min(TB, nT - t0)), new_ = max(0, min(EB, nE - e0));
       // (a) rows: lane r16 of tile j holds token item t0 + 16 j + r16 (steady
       // row, or a slot of its retrieved cluster found by binary search)
-      int rowj[NTILE];
+      // (the tiles' searches advance together: one LDS round trip per step)
+      int rowj[NTILE], pos[NTILE], tk[NTILE];
+      bool srch[NTILE];
 #pragma unroll
       for (int j = 0; j < NTILE; j++) {
         const int item = t0 + 16 * j + r16;
-        const int t = item - nS;
-        int pos = 0;
-        if (item < nT && t >= 0) {
+        tk[j] = item - nS;
+        srch[j] = item < nT && tk[j] >= 0;
+        pos[j] = 0;
+      }
 #pragma unroll 1
-          for (int s = s0; s > 0; s >>= 1)
-            if (pos + s < nR && Rtok[pos + s] <= t) pos += s;
-        }
+      for (int s = s0; s > 0; s >>= 1) {
+#pragma unroll
+        for (int j = 0; j < NTILE; j++)
+          if (srch[j] && pos[j] + s < nR && Rtok[pos[j] + s] <= tk[j]) pos[j] += s;
+      }
+#pragma unroll
+      for (int j = 0; j < NTILE; j++) {
+        const int item = t0 + 16 * j + r16;
         rowj[j] = item < nS ? s_lo + item
-                            : (item < nT ? (Rblk[pos] << lgT) + (t - Rtok[pos]) : 0);
+                            : (item < nT ? (Rblk[pos[j]] << lgT) + (tk[j] - Rtok[pos[j]]) : 0);
       }
       // cache slot of each retrieved row's block (-1: not cached)
       int slj[NTILE];
