@@ -107,7 +107,7 @@ def test_decode_full_budget_is_full_attention():
         assert rel_err(r["out"][0, hq], full[0, 0, 0].numpy()) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("G", [1, 7, 16])
+@pytest.mark.parametrize("G", [1, 2, 7, 8, 16])
 def test_decode_group_sizes(G):
     w = synth.custom(203 + G, "bf16", 2, 2 * G, 2, 68 + 3 * 512 + 100, 512, 32, n_needles=3,
                      anisotropic=(G == 7))
