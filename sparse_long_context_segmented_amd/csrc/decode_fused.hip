@@ -264,7 +264,6 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   __shared__ int rdx[256];
   __shared__ uint64_t rpref;
   __shared__ int rneed, s_last;
-  __shared__ float cden[MAX_G];
 
   // XCD-aware placement: the dispatcher deals consecutive workgroups round
   // robin to the 8 XCDs, so with a unit count that is a multiple of 8 the
@@ -1319,58 +1318,34 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   if (!s_last) return;
 
   // ---- 5. the last workgroup of the unit merges the W partials -------------
-  // A thread's accumulator loads for its first output element (one per
-  // partial; NV = 16, 32 or 64 >= W slots, slots v >= W repeat partial W - 1
-  // and get weight 0) are issued first, then the (m, l) of every partial; the
-  // weights e^{m_w - M} and the denominators are formed on chip. Every thread
-  // reaches both barriers.
+  // Wave by wave, with no workgroup barrier: a wave's 64 output elements
+  // belong to one head g. Its lanes load their elements' accumulators (one
+  // per partial; NV = 16, 32 or 64 >= W slots, slots v >= W repeat partial
+  // W - 1 and get weight 0) and, lane v, the (m, l) of partial v; the weights
+  // e^{m_v - M} and the denominator are formed across the wave and read back
+  // lane by lane.
   const float* pu = a.part + (int64_t)u * W * G * PART;
-  float* cm = reinterpret_cast<float*>(smem);  // [W][G] m
-  float* cl = cm + MAX_WG * MAX_G;             // [MAX_WG][G] l, then weights
   auto combine = [&](auto nv) {
     constexpr int NV = decltype(nv)::value;
-    auto acc_loads = [&](int e, float* av) {
-      const int g = e >> 7, t = e & (D - 1);
+#pragma unroll 1
+    for (int e0 = wv * 64; e0 < G * D; e0 += NT) {
+      const int g = e0 >> 7, t = (e0 & (D - 1)) + lane;
+      float av[NV];
 #pragma unroll
       for (int v = 0; v < NV; v++)
         av[v] = __hip_atomic_load(pu + ((int64_t)min(v, W - 1) * G + g) * PART + 2 + t,
                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    auto finish = [&](int e, const float* av) {
-      const int g = e >> 7, t = e & (D - 1);
+      const int64_t ml = ((int64_t)min(lane, W - 1) * G + g) * PART;
+      const float m0 = __hip_atomic_load(pu + ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float l0 = __hip_atomic_load(pu + ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float mv = lane < W ? m0 : -INFINITY;
+      const float M2 = wave_max_u(mv);
+      const float f = (mv == -INFINITY) ? 0.f : ex<DT>(mv - M2);  // weight of partial lane
+      const float den = wave_sum_u(f * (lane < W ? l0 : 0.f));
       float num = 0.f;
 #pragma unroll
-      for (int v = 0; v < NV; v++) num = fmaf(cl[v * G + g], av[v], num);
-      const float den = cden[g];
+      for (int v = 0; v < NV; v++) num = fmaf(rdlf(f, v), av[v], num);
       a.out[((int64_t)b * a.Hq + (int64_t)h * G + g) * D + t] = den > 0.f ? num / den : 0.f;
-    };
-    float av[NV];
-    const bool has = tid < G * D;
-    if (has) acc_loads(tid, av);
-    for (int i = tid; i < W * G; i += NT) {
-      cm[i] = __hip_atomic_load(pu + (int64_t)i * PART, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-      cl[i] = __hip_atomic_load(pu + (int64_t)i * PART + 1, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    // wave g handles head g, lane v partial v (W <= MAX_WG = 64)
-#pragma unroll 1
-    for (int g = wv; g < G; g += NW) {
-      const float mv = lane < W ? cm[lane * G + g] : -INFINITY;
-      const float M2 = wave_max_u(mv);
-      const float f = (mv == -INFINITY) ? 0.f : ex<DT>(mv - M2);
-      const float lv = lane < W ? cl[lane * G + g] : 0.f;
-      const float den = wave_sum_u(f * lv);
-      cl[lane * G + g] = lane < W ? f : 0.f;  // weight
-      if (lane == 0) cden[g] = den;
-    }
-    __syncthreads();
-    if (has) finish(tid, av);
-#pragma unroll 1
-    for (int e = tid + NT; e < GS * D && e < G * D; e += NT) {
-      acc_loads(e, av);
-      finish(e, av);
     }
   };
   if (W <= 16) combine(std::integral_constant<int, 16>{});
