@@ -449,31 +449,15 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
     off = -lo * inv;
     stage_store(0, k4, true);
     if constexpr (BIG) {
-      // passes 1 .. NP-1: the keys of pass p + 1 (head groups of up to 4,
-      // whose registers allow a third buffer: also p + 2) load while pass p
-      // is counted
+      // passes 1 .. NP-1: pass p + 1 loads while pass p is counted
       uint4 kb[KPT / 4];
       key_load(1, k4);
-      if constexpr (GS == 4) {
-        uint4 kc[KPT / 4];
-        key_load(min(2, NP - 1), kb);
 #pragma unroll 1
-        for (int p = 1; p < NP; p += 3) {
-          key_load(min(p + 2, NP - 1), kc);
-          count_keys(p, k4);
-          key_load(min(p + 3, NP - 1), k4);
-          if (p + 1 < NP) count_keys(p + 1, kb);
-          key_load(min(p + 4, NP - 1), kb);
-          if (p + 2 < NP) count_keys(p + 2, kc);
-        }
-      } else {
-#pragma unroll 1
-        for (int p = 1; p < NP; p += 2) {
-          key_load(min(p + 1, NP - 1), kb);
-          count_keys(p, k4);
-          key_load(min(p + 2, NP - 1), k4);
-          if (p + 1 < NP) count_keys(p + 1, kb);
-        }
+      for (int p = 1; p < NP; p += 2) {
+        key_load(min(p + 1, NP - 1), kb);
+        count_keys(p, k4);
+        key_load(min(p + 2, NP - 1), k4);
+        if (p + 1 < NP) count_keys(p + 1, kb);
       }
     }
   }
@@ -670,26 +654,12 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedArgs a) {
   } else {
     uint4 ka[KPT / 4], kb[KPT / 4];
     key_load(0, ka);
-    if constexpr (GS == 4) {  // (two passes ahead, as for the histogram)
-      uint4 kc[KPT / 4];
-      key_load(min(1, NP - 1), kb);
 #pragma unroll 1
-      for (int p = 0; p < NP; p += 3) {
-        key_load(min(p + 2, NP - 1), kc);
-        cand_scan(p, ka);
-        key_load(min(p + 3, NP - 1), ka);
-        if (p + 1 < NP) cand_scan(p + 1, kb);
-        key_load(min(p + 4, NP - 1), kb);
-        if (p + 2 < NP) cand_scan(p + 2, kc);
-      }
-    } else {
-#pragma unroll 1
-      for (int p = 0; p < NP; p += 2) {
-        key_load(min(p + 1, NP - 1), kb);
-        cand_scan(p, ka);
-        key_load(min(p + 2, NP - 1), ka);
-        if (p + 1 < NP) cand_scan(p + 1, kb);
-      }
+    for (int p = 0; p < NP; p += 2) {
+      key_load(min(p + 1, NP - 1), kb);
+      cand_scan(p, ka);
+      key_load(min(p + 2, NP - 1), ka);
+      if (p + 1 < NP) cand_scan(p + 1, kb);
     }
   }
   __syncthreads();
