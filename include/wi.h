@@ -420,7 +420,8 @@ wi_status wi_decode_attention_noalloc(const wi_index_desc *desc,
 
 /* Measurement hook. wi_timing_start() makes every kernel launch issued by
  * this library on the calling thread be bracketed by two HIP events recorded
- * on the launch's own stream, until wi_timing_stop(). wi_timing_stop()
+ * on the launch's own stream (timing-only events, recorded without a
+ * system-scope memory fence), until wi_timing_stop(). wi_timing_stop()
  * synchronises those events and writes, for up to max_records launches in
  * issue order, the kernel's name id (see wi_kernel_name) and its duration in
  * milliseconds; it returns the number of launches recorded (which may exceed

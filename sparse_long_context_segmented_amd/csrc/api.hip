@@ -278,8 +278,10 @@ hipEvent_t take_event() {
     t_pool.pop_back();
     return e;
   }
+  // timing-only events: no system-scope fence when they are recorded, so the
+  // bracket adds no cache writeback/invalidate around the launch it times
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
