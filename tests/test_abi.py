@@ -320,3 +320,16 @@ def test_dense_and_recall_reject_invalid_calls(L):
     nob = wi.IndexBufs(*([0x100000] * 12))
     nob.assign = None
     assert rec(b=nob) == 1
+
+
+def test_timing_hook_host_side(L):
+    """The measurement hook with no launch in between records nothing and
+    makes no HIP call; kernel ids map to their names, others to "unknown"."""
+    assert L.wi_timing_start() == 0
+    assert L.wi_timing_stop(0, None, None) == 0
+    assert wi.timing_stop() == []  # (stopping twice is harmless)
+    assert L.wi_kernel_name(0).decode() == "zero"
+    names = {L.wi_kernel_name(i).decode() for i in range(64)}
+    assert {"score", "select_attend", "assign", "kpp_round"} <= names
+    assert L.wi_kernel_name(-1).decode() == "unknown"
+    assert L.wi_kernel_name(1 << 20).decode() == "unknown"

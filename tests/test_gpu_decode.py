@@ -275,3 +275,26 @@ def test_decode_graph_replay_matches_eager():
         other = wi.decode_attention(gix, dd, q2, ws=ws)  # eager work on the same workspace
         torch.cuda.synchronize()
         assert not np.array_equal(other.cpu().numpy().view(np.uint32), ref)
+
+
+def test_timing_hook_records_decode_launches_and_keeps_outputs():
+    """With the measurement hook on, a decode call records its two launches
+    (score, then select_attend) with positive durations, and its output is
+    bit-identical to the same call without the hook."""
+    w = synth.custom(2100, "bf16", 1, 8, 2, 68 + 2 * 512 + 40, 512, 32)
+    K, V, q = synth.gen_batch(w)
+    gd = wi.make_desc("bf16", w.batch, w.n_kv_heads, w.n_ctx, seg_len=w.seg_len,
+                      clusters_per_seg=w.clusters_per_seg, n_iters=2)
+    dev = torch.device("cuda:0")
+    ix = wi.build_index(gd, torch.from_numpy(K).to(dev, torch.bfloat16),
+                        torch.from_numpy(V).to(dev, torch.bfloat16))
+    qt = torch.from_numpy(q).to(dev, torch.bfloat16)
+    dd = wi.DecodeDesc(w.n_q_heads, 3, 20, 0.0, 0)
+    plain = wi.decode_attention(ix, dd, qt).clone()
+    torch.cuda.synchronize()
+    wi.timing_start()
+    timed = wi.decode_attention(ix, dd, qt)
+    recs = wi.timing_stop()
+    assert [n for n, _ in recs] == ["score", "select_attend"], recs
+    assert all(ms > 0.0 for _, ms in recs), recs
+    assert torch.equal(timed, plain)
