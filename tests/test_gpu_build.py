@@ -120,3 +120,30 @@ def test_build_deterministic():
     b = index_to_host(wi.build_index(gd, kt, vt))
     torch.cuda.synchronize()
     assert_index_equal(a, b)
+
+
+def _random_build_cases(n, seed=20261204):
+    """Seeded random small shapes: dtype, batch, KV heads, segment length (with
+    a ragged last segment), clusters per segment, Lloyd iterations, layer id
+    and K/V layout."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "f32" if i % 4 == 3 else "bf16"
+        B, H = int(rng.integers(1, 3)), int(rng.choice([1, 2, 3]))
+        seg = int(rng.choice([32, 96, 200, 512, 1024]))
+        k = int(rng.integers(1, min(512, seg) + 1))
+        n_idx = int(rng.integers(1, 4 * seg + 1))
+        iters = int(rng.integers(0, 5))
+        layer = int(rng.integers(0, 40))
+        cases.append((i, dtype, B, H, seg, k, 68 + n_idx, iters, layer, bool(i % 3 == 1)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_build_cases(10), ids=lambda c: f"rand{c[0]}")
+def test_build_random_small_shapes(case):
+    """Build parity on seeded random small shapes: every output bit-exact."""
+    i, dtype, B, H, seg, k, n_ctx, iters, layer, strided = case
+    w = synth.custom(800 + i, dtype, B, 4 * H, H, n_ctx, seg, k, n_iters=iters, n_needles=2)
+    got, ref, _ = _build_both(w, n_iters=iters, layer=layer, strided=strided)
+    assert_index_equal(got, ref)

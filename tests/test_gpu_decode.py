@@ -298,3 +298,35 @@ def test_timing_hook_records_decode_launches_and_keeps_outputs():
     assert [n for n, _ in recs] == ["score", "select_attend"], recs
     assert all(ms > 0.0 for _, ms in recs), recs
     assert torch.equal(timed, plain)
+
+
+def _random_cases(n, seed=20261203):
+    """Seeded random small shapes: dtype, batch, KV heads, group size, segment
+    length (with a ragged last segment), clusters per segment, budgets and
+    workgroups per unit."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "f32" if i % 5 == 4 else "bf16"
+        B, H = int(rng.integers(1, 4)), int(rng.choice([1, 2, 3, 5]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 16]))
+        seg = int(rng.choice([64, 96, 128, 256, 1000]))
+        k = int(rng.integers(1, min(64, seg) + 1))
+        n_idx = int(rng.integers(1, 5 * seg + 1))
+        full, rem = divmod(n_idx, seg)
+        C = full * min(k, seg) + (min(k, rem) if rem else 0)
+        k_r = int(rng.integers(0, C + 1))
+        k_e = int(rng.integers(0, C + 1))
+        wg = int(rng.choice([0, 1, 3]))
+        cases.append((i, dtype, B, H, G, seg, k, 68 + n_idx, k_r, k_e, wg))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(16), ids=lambda c: f"rand{c[0]}")
+def test_decode_random_small_shapes(case):
+    """Decode parity on seeded random small shapes (selection, execution list
+    and output against the oracle, as in every decode test)."""
+    i, dtype, B, H, G, seg, k, n_ctx, k_r, k_e, wg = case
+    w = synth.custom(700 + i, dtype, B, H * G, H, n_ctx, seg, k, n_needles=2)
+    r = _run(w, k_r, k_e, wg=wg)
+    assert r["err"] <= TOL[dtype]
