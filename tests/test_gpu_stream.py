@@ -302,3 +302,42 @@ def test_prefill_chunked_build_equals_one_shot_llama8b_128k():
         assert np.array_equal(a[key], b[key]), key
     print(f"  {chunks} chunks, 15 segments clustered as they filled: {dt * 1e3:.0f} ms "
           f"(index bit-identical to the one-shot build)", flush=True)
+
+
+def _random_stream_cases(n, seed=20261206):
+    """Seeded random small streams: dtype, batch, KV heads, group size, sink and
+    local window sizes, segment length, clusters per segment, prefix length
+    (ragged), number of appended tokens (at least one extension) and budgets."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "f32" if i % 3 == 1 else "bf16"
+        B, H = int(rng.integers(1, 3)), int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 4, 7, 16]))
+        n_sink, n_local = (0, 1, 4)[i % 3], int(rng.choice([0, 5, 64]))
+        seg = int(rng.choice([32, 64, 96]))
+        k = int(rng.integers(1, min(24, seg) + 1))
+        n_ctx = n_sink + n_local + int(rng.integers(1, 3 * seg + 1))
+        n_new = int(rng.integers(seg + 1, 2 * seg + 1))  # the window is full: >= 1 extension
+        n_ctx += max(0, 69 - n_ctx - n_new)  # (the generator wants streams of 69+ tokens)
+        k_r, k_e = int(rng.integers(0, 6)), int(rng.integers(0, 20))
+        cases.append((i, dtype, B, H, G, n_sink, n_local, seg, k, n_ctx, n_new, k_r, k_e))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_stream_cases(6), ids=lambda c: f"rand{c[0]}")
+def test_stream_random_small_shapes(case):
+    """Seeded random streams, every step checked: steady and pending rows bit
+    for bit, every extension's index bit for bit, each decode like any decode."""
+    i, dtype, B, H, G, n_sink, n_local, seg, k, n_ctx, n_new, k_r, k_e = case
+    w = synth.custom(950 + i, dtype, B, H * G, H, n_ctx + n_new, seg, k, n_iters=2,
+                     n_needles=2, n_components=24)
+    K, V, q = synth.gen_batch(w)
+    s = Stream(w, K, V, n_ctx, n_sink, n_local)
+    for t in range(n_new):
+        s.step()
+        s.check_rows()
+        s.decode(_query(q, t, dtype), k_r, k_e, check_plain=(t == 0))
+    assert s.extensions >= 1
+    print(f"  {n_new} steps, {s.extensions} extensions, within {s.worst:.3e}, "
+          f"near-tie reorders {s.reorders}", flush=True)

@@ -114,3 +114,36 @@ def test_wave_buffer_llama8b_128k_batch1():
     drifting decode steps, tables checked every 8 steps."""
     h, m, S = _run(synth.WORKLOADS[1], 0.10, 24, check_every=8)
     print(f"  128K b1, {S} slots per unit: hit rate {h / (h + m):.3f}", flush=True)
+
+
+def _random_wb_cases(n, seed=20261205):
+    """Seeded random small shapes for the wave buffer: dtype, batch, KV heads,
+    group size, segment length (ragged last segment), clusters per segment,
+    retrieval budget, cache size as a share of the used blocks, steps."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "f32" if i % 3 == 2 else "bf16"
+        B, H = int(rng.integers(1, 3)), int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 4, 7, 8, 16]))
+        seg = int(rng.choice([128, 256, 512]))
+        k = int(rng.integers(4, min(64, seg) + 1))
+        n_idx = int(rng.integers(seg, 4 * seg + 1))
+        full, rem = divmod(n_idx, seg)
+        C = full * k + min(k, rem)
+        k_r = int(rng.integers(1, max(2, C // 3)))
+        frac = float(rng.choice([0.01, 0.1, 0.5, 1.0]))
+        steps = int(rng.integers(3, 9))
+        cases.append((i, dtype, B, H, G, seg, k, 68 + n_idx, k_r, frac, steps))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_wb_cases(8), ids=lambda c: f"rand{c[0]}")
+def test_wave_buffer_random_small_shapes(case):
+    """Seeded random shapes: every step's output equals the HBM decode bit for
+    bit, and the cache state equals the reference model's."""
+    i, dtype, B, H, G, seg, k, n_ctx, k_r, frac, steps = case
+    w = synth.custom(900 + i, dtype, B, H * G, H, n_ctx, seg, k, n_iters=2, n_needles=2,
+                     k_retrieve=k_r, n_components=64)
+    h, m, S = _run(w, frac, steps)
+    print(f"  {dtype} slots {S}: hits {h}, misses {m}", flush=True)
